@@ -1,0 +1,21 @@
+"""fp64 CPU oracle for paged-KV attention. TEST INFRASTRUCTURE: imported only by the tests,
+the smoke check and the benchmark's CPU baseline; never by the HIP library or its binding."""
+from . import paged_attention  # noqa: F401
+from .paged_attention import (  # noqa: F401
+    BLOCK_SIZE,
+    to_float64,
+    empty_pool,
+    slot_location,
+    write_kv,
+    blocks_for,
+    gather_logical,
+    kv_head_of,
+    last_key,
+    softmax_weights,
+    attend,
+    default_scale,
+    decode,
+    prefill_chunk,
+    split_kv_decode,
+    gather_kv,
+)
