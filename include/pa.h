@@ -1,0 +1,193 @@
+/*
+ * pa.h - C ABI of the MI355X (gfx950) paged-KV attention library, libpa.so.
+ *
+ * The KV cache is one pool of fixed-size blocks of 16 tokens; every request
+ * owns a block table mapping its logical token positions to physical blocks,
+ * which need not be contiguous and may be shared between requests (arcyou
+ * teardown of vLLM paged attention, section "PagedAttention: the KV cache is
+ * paged, like virtual memory"; kenhuang vLLM course, "Introduction", section
+ * "PagedAttention (intuition)"). Attention is handed the block table and
+ * gathers K/V from wherever the blocks live. One scheduler step mixes decode
+ * tokens and chunks of long prompts (arcyou teardown, section "Continuous
+ * batching: rebuild the batch every step"), so the library offers three
+ * calls that one step issues in order on one stream:
+ *   pa_write_kv       new tokens' K/V into their slots,
+ *   pa_prefill_chunk  causal attention of prompt chunks over cached + new K/V,
+ *   pa_decode         one query per request over its whole context.
+ *
+ * Conventions for every call
+ *   - Pointers named k_cache/v_cache/key/value/q/out/workspace and the int32
+ *     metadata arrays are DEVICE pointers owned by the caller; every tensor is
+ *     dense and row-major in the layout stated below. The library allocates no
+ *     device memory and keeps no state between calls.
+ *   - Pool layout, K and V alike: [num_blocks][16][num_kv_heads][head_dim].
+ *     Token t of a request lives in block block_table[t / 16] at offset t % 16.
+ *     A flat slot is block_id * 16 + offset.
+ *   - Element type: every tensor of a call (q, K/V pool, new K/V, out) has the
+ *     descriptor's dtype: PA_F32 (IEEE float32) or PA_BF16 (bfloat16 bits).
+ *     Arithmetic is float32; bf16 outputs are rounded to nearest, ties to even.
+ *   - Grouped-query attention: query head h reads kv head h / (Hq / Hkv).
+ *   - `stream` is a hipStream_t (NULL = the default stream). Calls only enqueue
+ *     work; they never synchronise, except in check mode (below).
+ *   - Return value: PA_OK or a negative pa_status. Argument errors are found
+ *     before anything is enqueued; pa_last_error_detail() then names the
+ *     argument. PA_ERR_HIP means the HIP runtime refused a launch.
+ *   - Content preconditions (block ids in [0, num_blocks), slots in range and
+ *     distinct, lengths within the stated maxima) are checked on the host only
+ *     when the environment variable PA_CHECK=1 is set: the call then
+ *     synchronises, copies the metadata to the host, and returns PA_ERR_RANGE
+ *     on a violation. Without check mode the kernels still never access memory
+ *     outside the pool: an out-of-range block id makes the affected outputs NaN,
+ *     an out-of-range slot is skipped, and lengths are clamped to the maxima.
+ *   - Calls on distinct streams may run concurrently; `out` must not alias an
+ *     input; a pa_write_kv must not target a block that another request still
+ *     reads (shared blocks are copied before they are written).
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_VERSION 10000 /* major*10000 + minor*100 + patch */
+#define PA_BLOCK_SIZE 16
+
+typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = -1, /* null pointer, non-positive size, inconsistent sizes */
+  PA_ERR_UNSUPPORTED = -2, /* shape or dtype this build has no kernel for */
+  PA_ERR_WORKSPACE = -3,   /* decode workspace missing or too small */
+  PA_ERR_RANGE = -4,       /* check mode found metadata outside its range */
+  PA_ERR_HIP = -5          /* the HIP runtime reported an error */
+} pa_status;
+
+/* One layer's KV pool. Supported: block_size 16; head_dim 64 or 128;
+ * num_q_heads a multiple of num_kv_heads with group G = Hq/Hkv; for PA_BF16
+ * G must be one of 1, 2, 4, 8, 16; for PA_F32 G <= 16 (decode only). */
+typedef struct {
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t block_size;
+  int64_t num_blocks;
+  int32_t dtype; /* pa_dtype */
+  int32_t reserved; /* must be 0 */
+} pa_cache_desc;
+
+/* Write new tokens' K and V into their slots (the "reshape and cache" step).
+ * The KV cache grows one token at a time: each new token's K/V rows are
+ * stored once, then read by every later token (arcyou teardown, section
+ * "The problem both ideas solve"; kenhuang, "PagedAttention (intuition)").
+ *   key, value     [num_tokens][Hkv][D]   new tokens, read only
+ *   k_cache/v_cache pool tensors, updated in place; only the addressed rows change
+ *   slot_mapping   int32 [num_tokens]; slot_mapping[i] = block*16 + offset, or -1
+ *                  to skip token i. Slots must be distinct within a call.
+ * The copy is bit-exact (no dtype change). num_tokens == 0 is a no-op. */
+int pa_write_kv(const pa_cache_desc* desc, const void* key, const void* value,
+                void* k_cache, void* v_cache, const int32_t* slot_mapping,
+                int64_t num_tokens, void* stream);
+
+/* Keys per split-KV partition that pa_decode chooses when partition_tokens is 0
+ * (a multiple of 16), for num_seqs requests of at most max_context_len tokens.
+ * The environment variable PA_PARTITION_TOKENS, if set, overrides the choice.
+ * Returns a negative pa_status on invalid arguments. */
+int32_t pa_decode_partition_tokens(const pa_cache_desc* desc, int32_t num_seqs,
+                                   int32_t max_context_len);
+
+/* Bytes of device workspace pa_decode needs for these sizes and this partition
+ * size (0 = automatic). 0 means no workspace is needed. Returns 0 for invalid
+ * arguments as well; pa_decode reports those. */
+size_t pa_decode_workspace_size(const pa_cache_desc* desc, int32_t num_seqs,
+                                int32_t max_context_len, int32_t partition_tokens);
+
+/* Decode attention: one query per request, at its last position, attending all
+ * context_lens[s] tokens of its logical context through its block table
+ * (arcyou teardown, section "PagedAttention: the KV cache is paged, like
+ * virtual memory": the kernel receives a per-request block table and gathers
+ * K/V wherever the blocks live). context_lens[s] counts the request's own
+ * newest token, whose K/V must already be written.
+ *   out            [num_seqs][Hq][D]  written
+ *   q              [num_seqs][Hq][D]
+ *   block_tables   int32 [num_seqs][max_blocks_per_seq]; entries at index
+ *                  >= ceil(context_lens[s]/16) are never read
+ *   context_lens   int32 [num_seqs], 1 <= context_lens[s] <= max_context_len;
+ *                  a length <= 0 yields NaN outputs for that request
+ *   max_context_len <= 16 * max_blocks_per_seq
+ *   scale          multiplies q.k before the softmax (normally 1/sqrt(D))
+ *   partition_tokens keys per split-KV partition: 0 = automatic, else a
+ *                  positive multiple of 16. A request longer than one partition
+ *                  is processed as several partial softmaxes that a second
+ *                  kernel merges.
+ *   workspace      device scratch of at least pa_decode_workspace_size(...)
+ *                  bytes for the same num_seqs, max_context_len and
+ *                  partition_tokens; may be NULL when that size is 0. Its
+ *                  contents on entry do not matter; concurrent calls need
+ *                  separate workspaces.
+ * num_seqs == 0 is a no-op. */
+int pa_decode(const pa_cache_desc* desc, void* out, const void* q, const void* k_cache,
+              const void* v_cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+              const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
+              float scale, int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+              void* stream);
+
+/* Causal attention for chunks of new tokens (chunked prefill) over the cached
+ * tokens plus the chunk itself. A long prompt may be split across steps and a
+ * chunk continues after the tokens already computed (arcyou teardown, section
+ * "Continuous batching: rebuild the batch every step"); the chunk's K/V must
+ * already be written. Row i of request s's chunk of n_s rows sits at absolute
+ * position seq_lens[s] - n_s + i and attends keys 0 .. that position.
+ * PA_BF16 only.
+ *   out, q         [num_tokens][Hq][D]; request s owns rows
+ *                  query_start_loc[s] .. query_start_loc[s+1]-1
+ *   query_start_loc int32 [num_seqs+1], non-decreasing, query_start_loc[0] = 0,
+ *                  query_start_loc[num_seqs] = num_tokens
+ *   seq_lens       int32 [num_seqs], total context including the chunk;
+ *                  n_s <= seq_lens[s] <= max_seq_len, n_s <= max_query_len
+ *   block_tables   int32 [num_seqs][max_blocks_per_seq]
+ *   max_seq_len    <= 16 * max_blocks_per_seq
+ * Requests with an empty chunk are skipped. num_seqs == 0 is a no-op. */
+int pa_prefill_chunk(const pa_cache_desc* desc, void* out, const void* q,
+                     const void* k_cache, const void* v_cache, const int32_t* query_start_loc,
+                     const int32_t* seq_lens, const int32_t* block_tables,
+                     int32_t max_blocks_per_seq, int32_t num_seqs, int32_t num_tokens,
+                     int32_t max_query_len, int32_t max_seq_len, float scale, void* stream);
+
+/* Copy each request's logical K and V out of the pool through its block table,
+ * bit for bit, using the same addressing as the attention kernels (an
+ * inspection aid for tests).
+ *   dst_k, dst_v   [num_seqs][max_context_len][Hkv][D]; rows t >= context_lens[s]
+ *                  are left untouched. */
+int pa_gather_kv(const pa_cache_desc* desc, void* dst_k, void* dst_v, const void* k_cache,
+                 const void* v_cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                 const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
+                 void* stream);
+
+/* Static text for a status code. */
+const char* pa_strerror(int status);
+/* Thread-local text naming what the last failing call on this thread rejected. */
+const char* pa_last_error_detail(void);
+/* PA_VERSION of the built library. */
+int pa_version(void);
+
+/* ---- Measurement utilities (not part of attention) ----------------------
+ * pa_bench_copy  copies `bytes` (a multiple of 16) from src to dst, 16 B per lane:
+ *                a plain streaming kernel of known traffic.
+ * pa_bench_read  reads `bytes` (a multiple of 16) from src and writes one word
+ *                per workgroup into sink (>= 4096 floats): the read ceiling.
+ * pa_bench_flush overwrites `bytes` (a multiple of 16) of buf, e.g. to evict
+ *                the last-level cache between timed runs. */
+int pa_bench_copy(void* dst, const void* src, size_t bytes, void* stream);
+int pa_bench_read(const void* src, size_t bytes, float* sink, void* stream);
+int pa_bench_flush(void* buf, size_t bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

@@ -1,0 +1,358 @@
+// pa_api.hip - the C ABI declared in include/pa.h: argument validation, the
+// optional host-side content check (PA_CHECK=1), split-KV sizing, and kernel
+// dispatch on the caller's stream. No device memory is allocated here.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdlib>
+#include <string>
+#include <unordered_set>
+#include <vector>
+
+#include "pa.h"
+#include "pa_device.h"
+
+namespace {
+
+thread_local std::string g_detail;
+
+int fail(int status, const std::string& what) {
+  g_detail = what;
+  return status;
+}
+
+bool check_mode() {
+  static const bool on = [] {
+    const char* e = std::getenv("PA_CHECK");
+    return e != nullptr && e[0] == '1';
+  }();
+  return on;
+}
+
+int elem_bytes(int32_t dtype) { return dtype == PA_BF16 ? 2 : 4; }
+
+int validate_desc(const pa_cache_desc* d) {
+  if (d == nullptr) return fail(PA_ERR_INVALID_ARG, "desc is NULL");
+  if (d->reserved != 0) return fail(PA_ERR_INVALID_ARG, "desc.reserved must be 0");
+  if (d->num_q_heads <= 0 || d->num_kv_heads <= 0)
+    return fail(PA_ERR_INVALID_ARG, "head counts must be positive");
+  if (d->num_q_heads % d->num_kv_heads != 0)
+    return fail(PA_ERR_INVALID_ARG, "num_q_heads must be a multiple of num_kv_heads");
+  if (d->num_blocks <= 0) return fail(PA_ERR_INVALID_ARG, "num_blocks must be positive");
+  if (d->num_blocks > (int64_t)INT32_MAX / PA_BLOCK_SIZE)
+    return fail(PA_ERR_UNSUPPORTED, "num_blocks * 16 must fit in int32 slots");
+  if (d->block_size != PA_BLOCK_SIZE) return fail(PA_ERR_UNSUPPORTED, "block_size must be 16");
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(PA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (d->dtype != PA_F32 && d->dtype != PA_BF16) return fail(PA_ERR_UNSUPPORTED, "unknown dtype");
+  const int g = d->num_q_heads / d->num_kv_heads;
+  if (d->dtype == PA_BF16 && g != 1 && g != 2 && g != 4 && g != 8 && g != 16)
+    return fail(PA_ERR_UNSUPPORTED, "bf16 kernels need q heads per kv head in {1,2,4,8,16}");
+  if (d->dtype == PA_F32 && g > 16)
+    return fail(PA_ERR_UNSUPPORTED, "fp32 kernels need at most 16 q heads per kv head");
+  return PA_OK;
+}
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return PA_OK;
+  return fail(PA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+template <class T>
+bool fetch(std::vector<T>& host, const void* dev, size_t count) {
+  host.resize(count);
+  if (count == 0) return true;
+  return hipMemcpy(host.data(), dev, count * sizeof(T), hipMemcpyDeviceToHost) == hipSuccess;
+}
+
+// Check that the blocks holding tokens 0..len-1 of every request are in the pool.
+int check_tables(const std::vector<int32_t>& tables, int32_t max_blocks,
+                 const std::vector<int32_t>& lens, int64_t num_blocks) {
+  for (size_t s = 0; s < lens.size(); ++s) {
+    const int nb = (lens[s] + PA_BLOCK_SIZE - 1) / PA_BLOCK_SIZE;
+    for (int b = 0; b < nb; ++b) {
+      const int32_t id = tables[s * (size_t)max_blocks + b];
+      if (id < 0 || id >= num_blocks)
+        return fail(PA_ERR_RANGE, "block_tables[" + std::to_string(s) + "][" + std::to_string(b) +
+                                      "] = " + std::to_string(id) + " is outside the pool");
+    }
+  }
+  return PA_OK;
+}
+
+int32_t env_partition() {
+  const char* e = std::getenv("PA_PARTITION_TOKENS");
+  if (e == nullptr) return 0;
+  const int v = std::atoi(e);
+  return (v > 0 && v % PA_BLOCK_SIZE == 0) ? v : 0;
+}
+
+// Partition size: the largest of 4096..256 keys that still yields at least
+// ~16 wavefronts per compute unit (256 CUs) if every request had the maximum
+// length; at least 256 keys, and no split when one partition covers all.
+int32_t choose_partition(const pa_cache_desc* d, int32_t num_seqs, int32_t max_context_len) {
+  const int32_t forced = env_partition();
+  if (forced > 0) return forced;
+  const int64_t target = 4096;
+  const int64_t units = (int64_t)num_seqs * d->num_kv_heads;
+  for (int32_t p = 4096; p >= 256; p >>= 1) {
+    const int64_t parts = ((int64_t)max_context_len + p - 1) / p;
+    if (units * parts >= target) return p;
+  }
+  return 256;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct DecodeLayout {
+  int32_t partition;
+  int32_t max_parts;
+  size_t acc_bytes;
+  size_t total;
+};
+
+DecodeLayout decode_layout(const pa_cache_desc* d, int32_t num_seqs, int32_t max_context_len,
+                           int32_t partition_tokens) {
+  DecodeLayout l{};
+  l.partition = partition_tokens > 0 ? partition_tokens
+                                     : choose_partition(d, num_seqs, max_context_len);
+  l.max_parts = (int32_t)(((int64_t)max_context_len + l.partition - 1) / l.partition);
+  if (l.max_parts <= 1) return l;
+  const size_t rows = (size_t)num_seqs * d->num_q_heads * l.max_parts;
+  l.acc_bytes = align256(rows * d->head_dim * sizeof(float));
+  l.total = l.acc_bytes + align256(rows * 2 * sizeof(float));
+  return l;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_version(void) { return PA_VERSION; }
+
+const char* pa_strerror(int status) {
+  switch (status) {
+    case PA_OK: return "success";
+    case PA_ERR_INVALID_ARG: return "invalid argument";
+    case PA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case PA_ERR_WORKSPACE: return "decode workspace missing or too small";
+    case PA_ERR_RANGE: return "metadata out of range (check mode)";
+    case PA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* pa_last_error_detail(void) { return g_detail.c_str(); }
+
+int pa_write_kv(const pa_cache_desc* desc, const void* key, const void* value, void* k_cache,
+                void* v_cache, const int32_t* slot_mapping, int64_t num_tokens, void* stream) {
+  int st = validate_desc(desc);
+  if (st != PA_OK) return st;
+  if (num_tokens < 0) return fail(PA_ERR_INVALID_ARG, "num_tokens is negative");
+  if (num_tokens == 0) return PA_OK;
+  if (!key || !value || !k_cache || !v_cache || !slot_mapping)
+    return fail(PA_ERR_INVALID_ARG, "null pointer argument");
+  const int row_bytes = desc->num_kv_heads * desc->head_dim * elem_bytes(desc->dtype);
+  const int64_t num_slots = desc->num_blocks * PA_BLOCK_SIZE;
+  if (check_mode()) {
+    if (hipStreamSynchronize(as_stream(stream)) != hipSuccess)
+      return fail(PA_ERR_HIP, "stream synchronize failed");
+    std::vector<int32_t> slots;
+    if (!fetch(slots, slot_mapping, (size_t)num_tokens)) return fail(PA_ERR_HIP, "copy of slots failed");
+    std::unordered_set<int32_t> seen;
+    for (int64_t i = 0; i < num_tokens; ++i) {
+      const int32_t s = slots[i];
+      if (s == -1) continue;
+      if (s < 0 || s >= num_slots)
+        return fail(PA_ERR_RANGE, "slot_mapping[" + std::to_string(i) + "] = " + std::to_string(s) +
+                                      " is outside the pool");
+      if (!seen.insert(s).second)
+        return fail(PA_ERR_RANGE, "slot " + std::to_string(s) + " is written twice");
+    }
+  }
+  return hip_status(pa::launch_write_kv(key, value, k_cache, v_cache, slot_mapping, num_tokens,
+                                        row_bytes, num_slots, as_stream(stream)),
+                    "write_kv launch");
+}
+
+int32_t pa_decode_partition_tokens(const pa_cache_desc* desc, int32_t num_seqs,
+                                   int32_t max_context_len) {
+  int st = validate_desc(desc);
+  if (st != PA_OK) return st;
+  if (num_seqs < 0 || max_context_len < 0) return fail(PA_ERR_INVALID_ARG, "negative size");
+  return choose_partition(desc, num_seqs, max_context_len);
+}
+
+size_t pa_decode_workspace_size(const pa_cache_desc* desc, int32_t num_seqs,
+                                int32_t max_context_len, int32_t partition_tokens) {
+  if (validate_desc(desc) != PA_OK || num_seqs <= 0 || max_context_len <= 0 ||
+      partition_tokens < 0 || partition_tokens % PA_BLOCK_SIZE != 0)
+    return 0;
+  return decode_layout(desc, num_seqs, max_context_len, partition_tokens).total;
+}
+
+int pa_decode(const pa_cache_desc* desc, void* out, const void* q, const void* k_cache,
+              const void* v_cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+              const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
+              float scale, int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+              void* stream) {
+  int st = validate_desc(desc);
+  if (st != PA_OK) return st;
+  if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs is negative");
+  if (num_seqs == 0) return PA_OK;
+  if (num_seqs > 65535) return fail(PA_ERR_UNSUPPORTED, "num_seqs above 65535");
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
+    return fail(PA_ERR_INVALID_ARG, "null pointer argument");
+  if (max_blocks_per_seq <= 0) return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq must be positive");
+  if (max_context_len <= 0) return fail(PA_ERR_INVALID_ARG, "max_context_len must be positive");
+  if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * PA_BLOCK_SIZE)
+    return fail(PA_ERR_INVALID_ARG, "max_context_len exceeds 16 * max_blocks_per_seq");
+  if (partition_tokens < 0 || partition_tokens % PA_BLOCK_SIZE != 0)
+    return fail(PA_ERR_INVALID_ARG, "partition_tokens must be 0 or a positive multiple of 16");
+  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
+  const DecodeLayout lay = decode_layout(desc, num_seqs, max_context_len, partition_tokens);
+  if (lay.total > 0 && (workspace == nullptr || workspace_bytes < lay.total))
+    return fail(PA_ERR_WORKSPACE, "workspace needs " + std::to_string(lay.total) + " bytes");
+  if (check_mode()) {
+    if (hipStreamSynchronize(as_stream(stream)) != hipSuccess)
+      return fail(PA_ERR_HIP, "stream synchronize failed");
+    std::vector<int32_t> lens, tables;
+    if (!fetch(lens, context_lens, num_seqs) ||
+        !fetch(tables, block_tables, (size_t)num_seqs * max_blocks_per_seq))
+      return fail(PA_ERR_HIP, "copy of metadata failed");
+    for (int s = 0; s < num_seqs; ++s)
+      if (lens[s] < 1 || lens[s] > max_context_len)
+        return fail(PA_ERR_RANGE, "context_lens[" + std::to_string(s) + "] = " +
+                                      std::to_string(lens[s]) + " is outside [1, max_context_len]");
+    st = check_tables(tables, max_blocks_per_seq, lens, desc->num_blocks);
+    if (st != PA_OK) return st;
+  }
+  pa::DecodeArgs a{};
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.out = out;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.part_acc = lay.total ? (float*)workspace : nullptr;
+  a.part_ml = lay.total ? (float*)((char*)workspace + lay.acc_bytes) : nullptr;
+  a.num_blocks = desc->num_blocks;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_seqs = num_seqs;
+  a.max_context_len = max_context_len;
+  a.num_q_heads = desc->num_q_heads;
+  a.num_kv_heads = desc->num_kv_heads;
+  a.group = desc->num_q_heads / desc->num_kv_heads;
+  a.partition_tokens = lay.partition;
+  a.max_parts = lay.max_parts;
+  a.scale_log2 = scale * pa::kLog2e;
+  return hip_status(pa::launch_decode(a, desc->head_dim, desc->dtype == PA_BF16, as_stream(stream)),
+                    "decode launch");
+}
+
+int pa_prefill_chunk(const pa_cache_desc* desc, void* out, const void* q, const void* k_cache,
+                     const void* v_cache, const int32_t* query_start_loc, const int32_t* seq_lens,
+                     const int32_t* block_tables, int32_t max_blocks_per_seq, int32_t num_seqs,
+                     int32_t num_tokens, int32_t max_query_len, int32_t max_seq_len, float scale,
+                     void* stream) {
+  int st = validate_desc(desc);
+  if (st != PA_OK) return st;
+  if (desc->dtype != PA_BF16) return fail(PA_ERR_UNSUPPORTED, "prefill supports bf16 only");
+  if (num_seqs < 0 || num_tokens < 0 || max_query_len < 0 || max_seq_len < 0)
+    return fail(PA_ERR_INVALID_ARG, "negative size");
+  if (num_seqs == 0 || num_tokens == 0 || max_query_len == 0) return PA_OK;
+  if (!out || !q || !k_cache || !v_cache || !query_start_loc || !seq_lens || !block_tables)
+    return fail(PA_ERR_INVALID_ARG, "null pointer argument");
+  if (max_blocks_per_seq <= 0) return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq must be positive");
+  if ((int64_t)max_seq_len > (int64_t)max_blocks_per_seq * PA_BLOCK_SIZE)
+    return fail(PA_ERR_INVALID_ARG, "max_seq_len exceeds 16 * max_blocks_per_seq");
+  if (max_query_len > max_seq_len) return fail(PA_ERR_INVALID_ARG, "max_query_len exceeds max_seq_len");
+  if ((int64_t)num_seqs * desc->num_kv_heads > INT32_MAX)
+    return fail(PA_ERR_UNSUPPORTED, "num_seqs * num_kv_heads too large");
+  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
+  if (check_mode()) {
+    if (hipStreamSynchronize(as_stream(stream)) != hipSuccess)
+      return fail(PA_ERR_HIP, "stream synchronize failed");
+    std::vector<int32_t> qsl, lens, tables;
+    if (!fetch(qsl, query_start_loc, (size_t)num_seqs + 1) || !fetch(lens, seq_lens, num_seqs) ||
+        !fetch(tables, block_tables, (size_t)num_seqs * max_blocks_per_seq))
+      return fail(PA_ERR_HIP, "copy of metadata failed");
+    if (qsl[0] != 0 || qsl[num_seqs] != num_tokens)
+      return fail(PA_ERR_RANGE, "query_start_loc must start at 0 and end at num_tokens");
+    for (int s = 0; s < num_seqs; ++s) {
+      const int n = qsl[s + 1] - qsl[s];
+      if (n < 0 || n > max_query_len)
+        return fail(PA_ERR_RANGE, "chunk of request " + std::to_string(s) + " has " +
+                                      std::to_string(n) + " rows");
+      if (lens[s] < n || lens[s] > max_seq_len)
+        return fail(PA_ERR_RANGE, "seq_lens[" + std::to_string(s) + "] = " +
+                                      std::to_string(lens[s]) + " is inconsistent");
+    }
+    st = check_tables(tables, max_blocks_per_seq, lens, desc->num_blocks);
+    if (st != PA_OK) return st;
+  }
+  pa::PrefillArgs a{};
+  a.q = (const uint16_t*)q;
+  a.k = (const uint16_t*)k_cache;
+  a.v = (const uint16_t*)v_cache;
+  a.out = (uint16_t*)out;
+  a.query_start_loc = query_start_loc;
+  a.seq_lens = seq_lens;
+  a.block_tables = block_tables;
+  a.num_blocks = desc->num_blocks;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_seqs = num_seqs;
+  a.num_tokens = num_tokens;
+  a.max_query_len = max_query_len;
+  a.max_seq_len = max_seq_len;
+  a.num_q_heads = desc->num_q_heads;
+  a.num_kv_heads = desc->num_kv_heads;
+  a.scale_log2 = scale * pa::kLog2e;
+  return hip_status(pa::launch_prefill(a, desc->head_dim, desc->num_q_heads / desc->num_kv_heads,
+                                       as_stream(stream)),
+                    "prefill launch");
+}
+
+int pa_gather_kv(const pa_cache_desc* desc, void* dst_k, void* dst_v, const void* k_cache,
+                 const void* v_cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                 const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
+                 void* stream) {
+  int st = validate_desc(desc);
+  if (st != PA_OK) return st;
+  if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs is negative");
+  if (num_seqs == 0 || max_context_len == 0) return PA_OK;
+  if (num_seqs > 65535) return fail(PA_ERR_UNSUPPORTED, "num_seqs above 65535");
+  if (!dst_k || !dst_v || !k_cache || !v_cache || !block_tables || !context_lens)
+    return fail(PA_ERR_INVALID_ARG, "null pointer argument");
+  if (max_context_len < 0 || max_blocks_per_seq <= 0 ||
+      (int64_t)max_context_len > (int64_t)max_blocks_per_seq * PA_BLOCK_SIZE)
+    return fail(PA_ERR_INVALID_ARG, "max_context_len exceeds 16 * max_blocks_per_seq");
+  const int row_bytes = desc->num_kv_heads * desc->head_dim * elem_bytes(desc->dtype);
+  return hip_status(pa::launch_gather_kv(dst_k, dst_v, k_cache, v_cache, block_tables,
+                                         max_blocks_per_seq, context_lens, num_seqs,
+                                         max_context_len, row_bytes, desc->num_kv_heads,
+                                         desc->num_blocks, as_stream(stream)),
+                    "gather_kv launch");
+}
+
+int pa_bench_copy(void* dst, const void* src, size_t bytes, void* stream) {
+  if (!dst || !src || bytes % 16) return fail(PA_ERR_INVALID_ARG, "copy needs 16-byte multiples");
+  if (bytes == 0) return PA_OK;
+  return hip_status(pa::launch_bench_copy(dst, src, bytes, as_stream(stream)), "copy launch");
+}
+
+int pa_bench_read(const void* src, size_t bytes, float* sink, void* stream) {
+  if (!src || !sink || bytes % 16) return fail(PA_ERR_INVALID_ARG, "read needs 16-byte multiples");
+  if (bytes == 0) return PA_OK;
+  return hip_status(pa::launch_bench_read(src, bytes, sink, as_stream(stream)), "read launch");
+}
+
+int pa_bench_flush(void* buf, size_t bytes, void* stream) {
+  if (!buf || bytes % 16) return fail(PA_ERR_INVALID_ARG, "flush needs 16-byte multiples");
+  if (bytes == 0) return PA_OK;
+  return hip_status(pa::launch_bench_flush(buf, bytes, as_stream(stream)), "flush launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,130 @@
+// pa_device.h - device helpers shared by the gfx950 kernels, and the internal
+// launcher interface between the kernels and the C ABI in pa_api.hip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+constexpr int kBlock = 16;  // tokens per physical KV block
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// Element offset of the K/V row of (physical block, offset in block, kv head).
+// Every kernel that reads or writes the pool addresses it through this function.
+__device__ __forceinline__ int64_t kv_row(int32_t block_id, int offset, int kv_head,
+                                          int num_kv_heads, int head_dim) {
+  return ((int64_t)block_id * kBlock + offset) * (int64_t)(num_kv_heads * head_dim) +
+         (int64_t)kv_head * head_dim;
+}
+
+// Physical block holding logical token t of a request (its block-table row);
+// the caller range-checks the id before addressing the pool with it.
+__device__ __forceinline__ int32_t table_block(const int32_t* table_row, int t) {
+  return table_row[t >> 4];
+}
+
+__device__ __forceinline__ bool block_ok(int32_t id, int64_t num_blocks) {
+  return id >= 0 && (int64_t)id < num_blocks;
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
+  return __uint_as_float(b << 16);
+}
+
+// float -> bfloat16 bits, round to nearest with ties to even; NaN stays NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Two floats -> packed bf16 pair (low half = a), hardware round-to-nearest-even.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 v;
+  v[0] = (__bf16)a;
+  v[1] = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---------------------------------------------------------------- launchers
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  float* part_acc;  // [S][Hq][max_parts][D]
+  float* part_ml;   // [S][Hq][max_parts][2]: running max (log2 units), sum of exponentials
+  int64_t num_blocks;
+  int32_t max_blocks;
+  int32_t num_seqs;
+  int32_t max_context_len;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t group;
+  int32_t partition_tokens;
+  int32_t max_parts;
+  float scale_log2;  // scale * log2(e)
+};
+
+struct PrefillArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* out;
+  const int32_t* query_start_loc;
+  const int32_t* seq_lens;
+  const int32_t* block_tables;
+  int64_t num_blocks;
+  int32_t max_blocks;
+  int32_t num_seqs;
+  int32_t num_tokens;
+  int32_t max_query_len;
+  int32_t max_seq_len;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  float scale_log2;
+};
+
+hipError_t launch_write_kv(const void* key, const void* value, void* k_cache, void* v_cache,
+                           const int32_t* slots, int64_t num_tokens, int row_bytes,
+                           int64_t num_slots, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, int head_dim, bool bf16, hipStream_t stream);
+hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int group, hipStream_t stream);
+hipError_t launch_gather_kv(void* dst_k, void* dst_v, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, int32_t max_blocks,
+                            const int32_t* context_lens, int32_t num_seqs,
+                            int32_t max_context_len, int row_bytes, int num_kv_heads,
+                            int64_t num_blocks, hipStream_t stream);
+hipError_t launch_bench_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
+hipError_t launch_bench_read(const void* src, size_t bytes, float* sink, hipStream_t stream);
+hipError_t launch_bench_flush(void* buf, size_t bytes, hipStream_t stream);
+
+}  // namespace pa

@@ -1,0 +1,108 @@
+"""Helpers for the GPU parity tests: move a seeded workload onto the GPU and run it through
+the C ABI (via the ctypes binding); compare against the oracle."""
+import sys
+
+import numpy as np
+import torch
+
+import paged_kv_cache_245_amd as pa
+from workloads import POISON_BITS
+
+# bf16: max |gpu - oracle| and ||gpu - oracle|| / ||oracle||; fp32 likewise.
+TOL = {"bf16": (2e-2, 1e-2), "f32": (1e-4, 1e-5)}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def device_tensor(arr, dtype, device="cuda"):
+    """Storage bits (uint16 for bf16, float32 for f32) -> torch tensor on the GPU."""
+    if dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32))
+    return t.to(device)
+
+
+def host_bits(t):
+    """GPU tensor -> numpy storage bits (uint16 for bf16, float32 for f32)."""
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def as64(t):
+    return t.detach().to(torch.float64).cpu().numpy()
+
+
+def i32(a, device="cuda"):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(device)
+
+
+def desc_of(w):
+    s = w.spec
+    return pa.cache_desc(s.num_q_heads, s.num_kv_heads, s.head_dim, s.num_blocks, s.dtype)
+
+
+def poisoned_pool(w, device="cuda"):
+    s = w.spec
+    shape = s.pool_shape()
+    if s.dtype == "bf16":
+        return torch.full(shape, POISON_BITS["bf16"], dtype=torch.int16, device=device).view(torch.bfloat16)
+    return torch.full(shape, POISON_BITS["f32"], dtype=torch.int32, device=device).view(torch.float32)
+
+
+def write(w, d, k, v, kvw, device="cuda"):
+    if len(kvw.slot_mapping) == 0:
+        return
+    pa.pa_write_kv(d, device_tensor(kvw.key, w.spec.dtype, device),
+                   device_tensor(kvw.value, w.spec.dtype, device), k, v,
+                   i32(kvw.slot_mapping, device))
+
+
+def gpu_pools(w, include_step=True, device="cuda"):
+    """Pools on the GPU after set-up (and step) writes, all through pa_write_kv."""
+    d = desc_of(w)
+    k, v = poisoned_pool(w, device), poisoned_pool(w, device)
+    write(w, d, k, v, w.setup, device)
+    if include_step:
+        write(w, d, k, v, w.step_write, device)
+    return d, k, v
+
+
+def run_decode(w, d, k, v, partition_tokens=0, device="cuda", q=None, tables=None):
+    dec = w.decode
+    S = len(dec.context_lens)
+    q_t = device_tensor(dec.q, w.spec.dtype, device) if q is None else q
+    bt = i32(dec.block_tables if tables is None else tables, device)
+    lens = i32(dec.context_lens, device)
+    out = torch.empty_like(q_t)
+    ws = pa.decode_workspace(d, S, dec.max_context_len, partition_tokens, device)
+    pa.pa_decode(d, out, q_t, k, v, bt, lens, dec.max_context_len, w.scale, ws, partition_tokens)
+    torch.cuda.synchronize()
+    return out
+
+
+def run_prefill(w, d, k, v, device="cuda"):
+    p = w.prefill
+    q_t = device_tensor(p.q, w.spec.dtype, device)
+    out = torch.empty_like(q_t)
+    pa.pa_prefill_chunk(d, out, q_t, k, v, i32(p.query_start_loc, device), i32(p.seq_lens, device),
+                        i32(p.block_tables, device), p.max_query_len, p.max_seq_len, w.scale)
+    torch.cuda.synchronize()
+    return out
+
+
+def assert_close(got, ref, dtype, what=""):
+    """got (GPU output as float64 numpy) vs the oracle's float64 result."""
+    mx, rel = TOL[dtype]
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    err = np.abs(got - ref)
+    worst = float(err.max())
+    rrms = float(np.sqrt((err ** 2).sum() / (ref ** 2).sum()))
+    say(f"    {what}: max|err| {worst:.3e} (tol {mx}), rel rms {rrms:.3e} (tol {rel})")
+    assert worst <= mx, f"{what}: max abs error {worst} > {mx}"
+    assert rrms <= rel, f"{what}: relative rms error {rrms} > {rel}"

@@ -1,0 +1,78 @@
+"""Causal chunked-prefill attention on the GPU against the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_245_amd as pa
+import workloads
+from gpu_support import (as64, assert_close, desc_of, device_tensor, gpu_pools, i32, run_decode,
+                         run_prefill, say)
+from oracle_support import oracle_pools, oracle_prefill
+
+pytestmark = pytest.mark.gpu
+
+
+def check(w, what):
+    d, k, v = gpu_pools(w)
+    out = run_prefill(w, d, k, v)
+    ok, ov = oracle_pools(w)
+    assert_close(as64(out), oracle_prefill(w, ok, ov), "bf16", what)
+    return d, k, v, out
+
+
+def test_mixed_step_prefill_full():
+    say("  prefill config 4")
+    check(workloads.make(4), "config 4 prefill")
+
+
+def test_cached_edge_counts():
+    """Empty, one-token, block-misaligned and maximal cached prefixes."""
+    w = workloads.c4_mixed_step(seed=4, cached=[0, 1, 2047, 4096], num_decodes=2)
+    check(w, "cached {0,1,2047,4096}")
+
+
+@pytest.mark.parametrize("group,D", [(g, D) for g in (1, 2, 4, 8, 16) for D in (64, 128)])
+def test_shapes(group, D):
+    w = workloads.custom_prefill(300 + group + D, cached=[0, 5, 16, 100], new=[1, 70, 33, 129],
+                                 Hq=2 * group, Hkv=2, D=D, dtype="bf16")
+    check(w, f"G={group} D={D}")
+
+
+def test_chunk_matches_rows_of_whole_prompt():
+    whole = workloads.custom_prefill(51, cached=[0], new=[300], Hq=8, Hkv=2, D=128, dtype="bf16")
+    d, k, v = gpu_pools(whole)
+    full = as64(run_prefill(whole, d, k, v))
+    p = whole.prefill
+    for c in (1, 17, 160, 299):
+        q = device_tensor(p.q[c:], "bf16")
+        out = torch.empty_like(q)
+        pa.pa_prefill_chunk(d, out, q, k, v, i32([0, 300 - c]), i32([300]), i32(p.block_tables),
+                            300 - c, 300, whole.scale)
+        torch.cuda.synchronize()
+        assert_close(as64(out), full[c:], "bf16", f"chunk after {c}")
+
+
+def test_decode_is_a_one_row_chunk():
+    w = workloads.custom_decode(61, [1, 16, 17, 250, 1000], Hq=16, Hkv=2, D=128, dtype="bf16")
+    d, k, v = gpu_pools(w)
+    dec = as64(run_decode(w, d, k, v))
+    q = device_tensor(w.decode.q, "bf16")
+    out = torch.empty_like(q)
+    pa.pa_prefill_chunk(d, out, q, k, v, i32(np.arange(6)), i32(w.decode.context_lens),
+                        i32(w.decode.block_tables), 1, 1000, w.scale)
+    torch.cuda.synchronize()
+    assert np.max(np.abs(as64(out) - dec)) <= 2e-2
+
+
+def test_empty_chunk_is_skipped():
+    w = workloads.custom_prefill(71, cached=[3, 9], new=[20, 5], Hq=4, Hkv=2, D=64, dtype="bf16")
+    d, k, v = gpu_pools(w)
+    p = w.prefill
+    q = device_tensor(p.q, "bf16")
+    out = torch.zeros_like(q)
+    # request 0 gets an empty chunk (all 25 rows belong to request 1, which now has 25 new rows)
+    pa.pa_prefill_chunk(d, out, q[:5], k, v, i32([0, 0, 5]), i32([23, 14]), i32(p.block_tables),
+                        5, 23, w.scale)
+    torch.cuda.synchronize()
+    assert np.all(np.isfinite(as64(out[:5])))
+    assert not out[5:].any()
