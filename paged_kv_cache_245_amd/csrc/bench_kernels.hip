@@ -26,9 +26,19 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(u32x4* __restrict__ dst,
 
 __global__ __launch_bounds__(kThreads) void read_kernel(const u32x4* __restrict__ src,
                                                         int64_t n16, float* __restrict__ sink) {
+  // four independent 16-byte loads in flight per lane per iteration
   const int64_t step = (int64_t)gridDim.x * kThreads;
   uint32_t x = 0;
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n16; i += step) {
+  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  for (; i + 3 * step < n16; i += 4 * step) {
+    const u32x4 a = __builtin_nontemporal_load(src + i);
+    const u32x4 b = __builtin_nontemporal_load(src + i + step);
+    const u32x4 c = __builtin_nontemporal_load(src + i + 2 * step);
+    const u32x4 d = __builtin_nontemporal_load(src + i + 3 * step);
+    x ^= a[0] ^ a[1] ^ a[2] ^ a[3] ^ b[0] ^ b[1] ^ b[2] ^ b[3] ^ c[0] ^ c[1] ^ c[2] ^ c[3] ^
+         d[0] ^ d[1] ^ d[2] ^ d[3];
+  }
+  for (; i < n16; i += step) {
     const u32x4 v = __builtin_nontemporal_load(src + i);
     x ^= v[0] ^ v[1] ^ v[2] ^ v[3];
   }

@@ -4,43 +4,53 @@
 // "PagedAttention: the KV cache is paged, like virtual memory"; every new token
 // re-reads all past K/V: kenhuang vLLM course, "PagedAttention (intuition)").
 //
-// Work split. A request's context is cut into partitions of P keys (a multiple
-// of 16). One wavefront owns one (request, kv head, partition) and keeps a
-// running softmax over it: max m, sum of exponentials l and the unnormalised
-// output acc (the usual online-softmax recurrence). A request that fits in one
-// partition is finished in place; otherwise each partition stores (m, l, acc)
-// and decode_merge_kernel combines them: out = sum(2^(m_p-M) acc_p) /
-// sum(2^(m_p-M) l_p), M = max m_p. Scores are kept in log2 units (the scale is
-// pre-multiplied by log2 e) so every exponential is one v_exp_f32.
+// Decode is a stream over the pool: ~G flop per byte of K/V, far below the MFMA
+// or VALU ridge, so the design goal is that every compute unit streams K/V at
+// its full rate from the first to the last microsecond.
 //
-// bf16 kernel, per wavefront and per pair of 16-token blocks (32 keys):
-//   S^T[16 keys x 16 heads] = K[16 x D] . Q^T[D x 16]   (D/32 MFMA 16x16x32 per block)
-//     A operand = K rows: lane (n = lane%16, g4 = lane/16) loads 16 B of key n's
-//     row at d = 32c + 8 g4; a block of one kv head is 16 rows of 2*D bytes.
-//     B operand = the group's G query heads in columns 0..G-1 (columns >= G are 0).
-//     Result: lane holds the scores of head n for keys 4 g4 .. 4 g4 + 3.
-//   O^T[16 d x 16 heads] += V^T[16 d x 32 keys] . P^T[32 keys x 16 heads]
-//     (D/16 MFMA 16x16x32, one per 16 output d values)
+// Work split (balanced mode, the default). The requests' blocks are laid end to
+// end (request 0's blocks, then request 1's, ...), T blocks in all, and
+// workgroup w of W takes blocks [w*T/W, (w+1)*T/W): every workgroup gets the
+// same number of blocks whatever the length mix, and streams them in order.
+// A workgroup has one wavefront per kv head (up to 8), so together they read
+// whole token rows: a 16-token block of 8 kv heads x 128 dims is one contiguous
+// 32 KiB read. A workgroup's range is cut at request boundaries into segments;
+// each segment keeps an online softmax (running max m, sum of exponentials l,
+// unnormalised output acc). A segment that is a whole request writes the final
+// output; otherwise it stores (m, l, acc) in slot (request + worker), and a
+// merge kernel combines a request's slots: out = sum(2^(m_i-M) acc_i) /
+// sum(2^(m_i-M) l_i), M = max m_i. The slot index is unique because walking the
+// block axis, every segment boundary advances the request, the worker, or both,
+// so (request + worker) strictly increases from segment to segment.
+// Fixed-partition mode (an explicit partition size, or very large batches):
+// one workgroup per (request, partition of P keys, group of kv heads).
+//
+// Per wavefront and per pair of 16-token blocks (32 keys), with MFMA 16x16x32 bf16:
+//   S^T[16 keys x 16 heads] = K[16 x D] . Q^T[D x 16]     (D/32 MFMAs per block)
+//     A operand: lane (n = lane%16, g4 = lane/16) holds 8 dims of key n's row;
+//     B operand: the G query heads of this kv head in columns 0..G-1 (rest 0).
+//     Result: lane (n, g4) holds head n's scores for keys 4 g4 .. 4 g4 + 3.
+//   O^T[16 dims x 16 heads] += V^T[16 x 32 keys] . P^T[32 keys x 16 heads]
 //     B operand = the lane's own 8 probabilities (4 keys of each block), so the
-//     softmax output needs no cross-lane movement; the k index of the product
-//     is mapped to those 8 keys. A operand = the same 8 keys of V: the lane
-//     loads D/16 consecutive d values of each of the 8 rows (one 16-byte load
-//     per row for D=128) and transposes the 8 x (D/16) tile in registers.
-//     Output lane (n, g4) owns head n, d = (D/4) g4 .. (D/4) g4 + D/4 - 1.
-//   The probabilities are rounded to bf16 for the PV product; the running sum
-//   l uses the fp32 values.
-// K/V loads are 16 B per lane; for each row all its bytes are requested by the
-// same instruction group, so each 16-token block is fetched as 16 fully used
-// 2*D-byte segments. Block ids are wavefront-uniform scalar loads.
+//     softmax output never moves between lanes. A operand = V of those same 8
+//     keys: the lane loads D/16 consecutive dims of each of the 8 rows and
+//     transposes the 8 x (D/16) tile in registers. Lane (n, g4) ends up owning
+//     head n, dims (D/4) g4 .. (D/4) g4 + D/4 - 1.
+//   Probabilities are rounded to bf16 for the PV product; l sums the fp32 values.
+//   Scores are in log2 units (scale * log2 e), so each exponential is v_exp_f32.
+// The next pair's K/V is loaded before the current pair is used (two register
+// buffers), and a segment's block ids are fetched 64 at a time into one VGPR.
 //
-// fp32 kernel: a plain VALU kernel (lanes over keys for q.k, lanes over d for
-// PV) with the same partition / merge scheme, for fp32 pools.
+// fp32 pools use a plain VALU kernel (lanes over keys for q.k, lanes over dims
+// for PV) in fixed-partition mode.
+#include <cstdlib>
+
 #include "pa_device.h"
 
 namespace pa {
 namespace {
 
-constexpr int kDecodeWaves = 4;  // kv heads per workgroup in the bf16 kernel
+constexpr int kMaxBalancedSeqs = 8192;  // requests whose block prefix sums fit in LDS
 
 template <int D>
 struct VRowT;
@@ -49,38 +59,397 @@ struct VRowT<128> { typedef u32x4 type; };
 template <>
 struct VRowT<64> { typedef u32x2 type; };
 
-template <int D>
-__global__ __launch_bounds__(64 * kDecodeWaves) void decode_bf16_kernel(DecodeArgs a) {
-  static_assert(D == 64 || D == 128, "head_dim");
-  constexpr int kChunks = D / 32;  // MFMA k-chunks of q.k
-  constexpr int kDL = D / 16;      // d values per lane per V row == PV tiles
-  typedef typename VRowT<D>::type VRow;
+template <class T, bool kNT>
+__device__ __forceinline__ T load_kv(const uint16_t* p) {
+  if constexpr (kNT) return __builtin_nontemporal_load((const T*)p);
+  else return *(const T*)p;
+}
 
+// K and V of one pair of blocks as seen by one lane.
+template <int D>
+struct Tile {
+  u32x4 k0[D / 32], k1[D / 32];
+  typename VRowT<D>::type v[8];
+};
+
+// Byte offsets of one lane's K and V pieces inside a block (the same for every
+// block): K row n, dims 8 g4 + 32 c; V rows 4 g4 .. 4 g4 + 3, dims (D/16) n ...
+struct LaneOffsets {
+  uint32_t k;  // + 64 c for chunk c
+  uint32_t v;  // + j * row_bytes for row j
+  uint32_t row_bytes;
+};
+
+template <int D>
+__device__ __forceinline__ LaneOffsets lane_offsets(int kvh, int Hkv, int n, int g4) {
+  LaneOffsets o;
+  o.row_bytes = (uint32_t)(Hkv * D * 2);
+  o.k = (uint32_t)(kv_row(0, n, kvh, Hkv, D) * 2) + 16u * g4;
+  o.v = (uint32_t)(kv_row(0, 4 * g4, kvh, Hkv, D) * 2) + (uint32_t)(D / 16) * 2u * n;
+  return o;
+}
+
+template <int D, bool kNT>
+__device__ __forceinline__ void load_pair(Tile<D>& t, const uint16_t* K, const uint16_t* V,
+                                          int32_t id0, int32_t id1, bool two,
+                                          const LaneOffsets& o) {
+  typedef typename VRowT<D>::type VRow;
+  // wavefront-uniform block bases (the block id is a scalar), per-lane fixed offsets
+  const int64_t block_bytes = (int64_t)kBlock * o.row_bytes;
+  const char* kb0 = (const char*)K + (int64_t)id0 * block_bytes;
+  const char* vb0 = (const char*)V + (int64_t)id0 * block_bytes;
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c) t.k0[c] = load_kv<u32x4, kNT>((const uint16_t*)(kb0 + o.k + 64 * c));
+#pragma unroll
+  for (int j = 0; j < 4; ++j) t.v[j] = load_kv<VRow, kNT>((const uint16_t*)(vb0 + o.v + j * o.row_bytes));
+  if (two) {
+    const char* kb1 = (const char*)K + (int64_t)id1 * block_bytes;
+    const char* vb1 = (const char*)V + (int64_t)id1 * block_bytes;
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) t.k1[c] = load_kv<u32x4, kNT>((const uint16_t*)(kb1 + o.k + 64 * c));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) t.v[4 + j] = load_kv<VRow, kNT>((const uint16_t*)(vb1 + o.v + j * o.row_bytes));
+  } else {
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) t.k1[c] = u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) t.v[4 + j] = VRow{};
+  }
+}
+
+// Online-softmax update with one pair of blocks; `valid` = keys of the pair
+// (0..32, in order) that belong to the range being attended.
+template <int D>
+__device__ __forceinline__ void attend_pair(Tile<D>& t, const u32x4* qb, f32x4* acc, float& m,
+                                            float& lsum, float scale_log2, int valid, int g4) {
+  constexpr int kDL = D / 16;
+  typedef typename VRowT<D>::type VRow;
+  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c) {
+    s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(t.k0[c]), as_bf16x8(qb[c]), s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(t.k1[c]), as_bf16x8(qb[c]), s1, 0, 0, 0);
+  }
+  float sc[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    sc[i] = s0[i] * scale_log2;
+    sc[4 + i] = s1[i] * scale_log2;
+  }
+  if (valid < 32) {  // keys past the range: score -inf (by selection), V row 0
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if ((j >> 2) * 16 + 4 * g4 + (j & 3) >= valid) {
+        sc[j] = -INFINITY;
+        t.v[j] = VRow{};
+      }
+    }
+  }
+  float tmax = sc[0];
+#pragma unroll
+  for (int j = 1; j < 8; ++j) tmax = fmaxf(tmax, sc[j]);
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+  const float m_new = fmaxf(m, tmax);
+  const float alpha = fast_exp2(m - m_new);
+  float p[8];
+  float psum = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    p[j] = fast_exp2(sc[j] - m_new);
+    psum += p[j];
+  }
+  lsum = lsum * alpha + psum;
+  m = m_new;
+  const u32x4 pb = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                    pack_bf16x2(p[6], p[7])};
+#pragma unroll
+  for (int d = 0; d < kDL; ++d) {
+    u32x4 va;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t lo = t.v[2 * u][d >> 1];
+      const uint32_t hi = t.v[2 * u + 1][d >> 1];
+      va[u] = (d & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+    }
+    acc[d] *= alpha;
+    acc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va), as_bf16x8(pb), acc[d], 0, 0, 0);
+  }
+}
+
+// acc[d][i] of lane (n, g4) is dim (D/16) * (4 g4 + i) + d of head n.
+template <int D>
+__device__ __forceinline__ void store_final(uint16_t* O, int64_t qo_row, const f32x4* acc,
+                                            float lsum, int g4) {
+  constexpr int kDL = D / 16;
+  const float inv = 1.f / lsum;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint16_t* dst = O + qo_row + kDL * (4 * g4 + i);
+    if constexpr (D == 128) {
+      u32x4 w;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) w[t] = pack_bf16x2(acc[2 * t][i] * inv, acc[2 * t + 1][i] * inv);
+      *(u32x4*)dst = w;
+    } else {
+      u32x2 w;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) w[t] = pack_bf16x2(acc[2 * t][i] * inv, acc[2 * t + 1][i] * inv);
+      *(u32x2*)dst = w;
+    }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void store_partial(const DecodeArgs& a, int64_t pidx, const f32x4* acc,
+                                              float m, float lsum, int g4) {
+  constexpr int kDL = D / 16;
+  float* dst = a.part_acc + pidx * D;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int t4 = 0; t4 < kDL; t4 += 4)
+      *(f32x4*)(dst + kDL * (4 * g4 + i) + t4) =
+          f32x4{acc[t4][i], acc[t4 + 1][i], acc[t4 + 2][i], acc[t4 + 3][i]};
+  if (g4 == 0) {
+    a.part_ml[2 * pidx] = m;
+    a.part_ml[2 * pidx + 1] = lsum;
+  }
+}
+
+// One wavefront attends keys of blocks [blk_a, blk_b) of request s (kv head kvh),
+// keys limited to the first `end_tok` tokens, and writes the final output (whole)
+// or the partial state into partial row pidx_base + q head.
+template <int D, bool kNT>
+__device__ __forceinline__ void decode_segment(const DecodeArgs& a, int s, int kvh, int blk_a,
+                                               int blk_b, int end_tok, bool whole,
+                                               int64_t pidx_base, int64_t pidx_stride) {
+  constexpr int kChunks = D / 32;
+  constexpr int kDL = D / 16;
   const int lane = threadIdx.x & 63;
-  const int kvh = blockIdx.y * kDecodeWaves + (threadIdx.x >> 6);
+  const int n = lane & 15;
+  const int g4 = lane >> 4;
+  const int G = a.group;
+  const int Hkv = a.num_kv_heads;
+  const int h = kvh * G + n;
+  const bool head_ok = n < G;
+  const uint16_t* __restrict__ K = (const uint16_t*)a.k;
+  const uint16_t* __restrict__ V = (const uint16_t*)a.v;
+  const int64_t qo_row = ((int64_t)s * a.num_q_heads + h) * D;
+
+  u32x4 qb[kChunks];
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c)
+    qb[c] = head_ok ? *(const u32x4*)((const uint16_t*)a.q + qo_row + 32 * c + 8 * g4)
+                    : u32x4{0, 0, 0, 0};
+  f32x4 acc[kDL];
+#pragma unroll
+  for (int t = 0; t < kDL; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, lsum = 0.f;
+  bool poisoned = false;
+
+  // block ids of this segment, 64 per refill: lane i holds the id of block base + i
+  const int32_t* table = a.block_tables + (int64_t)s * a.max_blocks;
+  int base = blk_a;
+  int32_t idv = (lane < blk_b - base) ? table[base + lane] : 0;
+  auto block_id = [&](int b) -> int32_t {
+    if (b - base >= 64) {
+      base += 64;
+      idv = (lane < blk_b - base) ? table[base + lane] : 0;
+    }
+    int32_t id = __builtin_amdgcn_readlane(idv, b - base);
+    if (!block_ok(id, a.num_blocks)) {
+      poisoned = true;
+      id = 0;
+    }
+    return id;
+  };
+  const LaneOffsets offs = lane_offsets<D>(kvh, Hkv, n, g4);
+  auto issue = [&](Tile<D>& t, int b) {
+    const bool two = b + 1 < blk_b;
+    const int32_t id0 = block_id(b);
+    const int32_t id1 = two ? block_id(b + 1) : 0;
+    load_pair<D, kNT>(t, K, V, id0, id1, two, offs);
+  };
+
+  end_tok = min(end_tok, 16 * blk_b);  // a segment may stop before the request does
+  Tile<D> ta, tb;
+  int b = blk_a;
+  issue(ta, b);
+  while (true) {
+    if (b + 2 < blk_b) issue(tb, b + 2);
+    attend_pair<D>(ta, qb, acc, m, lsum, a.scale_log2, min(32, end_tok - 16 * b), g4);
+    b += 2;
+    if (b >= blk_b) break;
+    if (b + 2 < blk_b) issue(ta, b + 2);
+    attend_pair<D>(tb, qb, acc, m, lsum, a.scale_log2, min(32, end_tok - 16 * b), g4);
+    b += 2;
+    if (b >= blk_b) break;
+  }
+
+  lsum += __shfl_xor(lsum, 16, 64);
+  lsum += __shfl_xor(lsum, 32, 64);
+  if (poisoned) lsum = __builtin_nanf("");
+  if (!head_ok) return;
+  if (whole)
+    store_final<D>((uint16_t*)a.out, qo_row, acc, lsum, g4);
+  else
+    store_partial<D>(a, pidx_base + (int64_t)h * pidx_stride, acc, m, lsum, g4);
+}
+
+__device__ __forceinline__ int request_blocks(const DecodeArgs& a, int s) {
+  const int L = min(a.context_lens[s], a.max_context_len);
+  return L > 0 ? (L + 15) >> 4 : 0;
+}
+
+// Balanced mode: grid (W, kv-head groups); dynamic LDS holds S+1 ints.
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) void decode_bf16_balanced_kernel(DecodeArgs a) {
+  extern __shared__ int32_t cum[];
+  __shared__ int32_t wave_total[NW];
+  constexpr int kThreads = 64 * NW;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int S = a.num_seqs;
+
+  // prefix sums of blocks per request: each thread scans a contiguous run
+  const int per = (S + kThreads - 1) / kThreads;
+  const int r0 = min(tid * per, S), r1 = min(r0 + per, S);
+  int mine = 0;
+  for (int r = r0; r < r1; ++r) mine += request_blocks(a, r);
+  int incl = mine;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int up = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += up;
+  }
+  if (lane == 63) wave_total[wave] = incl;
+  __syncthreads();
+  int before = 0;
+  for (int i = 0; i < wave; ++i) before += wave_total[i];
+  int run = before + incl - mine;
+  for (int r = r0; r < r1; ++r) {
+    cum[r] = run;
+    run += request_blocks(a, r);
+  }
+  if (tid == kThreads - 1) cum[S] = run;
+  __syncthreads();
+  if (blockIdx.x == 0 && blockIdx.y == 0)
+    for (int r = tid; r <= S; r += kThreads) a.cum_blocks[r] = cum[r];
+
+  // Split over W = min(workgroups, T) workers, so that every worker owns at least
+  // one block (the merge relies on it); surplus workgroups idle.
+  const int64_t T = cum[S];
+  const int W = (int)min((int64_t)gridDim.x, T), w = blockIdx.x;
+  if (w >= W) return;
+  const int lo = (int)((int64_t)w * T / W), hi = (int)((int64_t)(w + 1) * T / W);
+  const int kvh = blockIdx.y * NW + wave;
+  if (lo >= hi || kvh >= a.num_kv_heads) return;  // no barrier after this point
+
+  // first request whose blocks reach past lo
+  int first = 0, last = S - 1;
+  while (first < last) {
+    const int mid = (first + last) >> 1;
+    if (cum[mid + 1] > lo) last = mid; else first = mid + 1;
+  }
+  // More attended blocks than the pool holds means blocks are shared (prefix
+  // sharing): keep them cacheable. Otherwise stream K/V past the caches.
+  const bool nt = a.nontemporal >= 0 ? a.nontemporal != 0 : T <= a.num_blocks;
+  int s = __builtin_amdgcn_readfirstlane(first);
+  int pos = lo;
+  while (pos < hi) {
+    const int cs = __builtin_amdgcn_readfirstlane(cum[s]);
+    const int ce = __builtin_amdgcn_readfirstlane(cum[s + 1]);
+    if (ce > pos) {
+      const int seg_end = min(ce, hi);
+      const int L = min(a.context_lens[s], a.max_context_len);
+      const bool whole = pos == cs && seg_end == ce;
+      const int64_t slot = (int64_t)s + w;
+      if (nt)
+        decode_segment<D, true>(a, s, kvh, pos - cs, seg_end - cs, L, whole,
+                                slot * a.num_q_heads, 1);
+      else
+        decode_segment<D, false>(a, s, kvh, pos - cs, seg_end - cs, L, whole,
+                                 slot * a.num_q_heads, 1);
+      pos = seg_end;
+    }
+    ++s;
+  }
+}
+
+// Worker holding global block b when T >= W blocks are split over W workers
+// (worker w owns blocks [w*T/W, (w+1)*T/W), never an empty range).
+__device__ __forceinline__ int worker_of(int64_t b, int64_t T, int W) {
+  return (int)(((b + 1) * W + T - 1) / T) - 1;
+}
+
+// Balanced mode merge: one wavefront per (q head, request); lanes own D/64 dims.
+template <int D>
+__global__ __launch_bounds__(64) void decode_merge_balanced_kernel(DecodeArgs a) {
+  constexpr int kE = D / 64;
+  const int lane = threadIdx.x;
+  const int h = blockIdx.x;
+  const int s = blockIdx.y;
+  uint16_t* O = (uint16_t*)a.out;
+  const int64_t orow = ((int64_t)s * a.num_q_heads + h) * D + kE * lane;
+  const int L = min(a.context_lens[s], a.max_context_len);
+  if (L <= 0) {
+#pragma unroll
+    for (int e = 0; e < kE; ++e) O[orow + e] = 0x7fc0;
+    return;
+  }
+  const int64_t T = a.cum_blocks[a.num_seqs];
+  const int W = (int)min((int64_t)a.num_workers, T);  // as in the decode kernel
+  const int w0 = worker_of(a.cum_blocks[s], T, W);
+  const int w1 = worker_of(a.cum_blocks[s + 1] - 1, T, W);
+  if (w0 == w1) return;  // one segment: written by the decode kernel
+  const int np = w1 - w0 + 1;
+  // partial of worker w0 + i for this (request, head) is row (s + w0 + i) * Hq + h
+  const int64_t row0 = ((int64_t)s + w0) * a.num_q_heads + h;
+  const int64_t rstep = a.num_q_heads;
+  float M = -INFINITY;
+  for (int i = lane; i < np; i += 64) M = fmaxf(M, a.part_ml[2 * (row0 + i * rstep)]);
+  M = wave_max(M);
+  float den = 0.f;
+  for (int i = lane; i < np; i += 64) {
+    const int64_t r = row0 + i * rstep;
+    den += fast_exp2(a.part_ml[2 * r] - M) * a.part_ml[2 * r + 1];
+  }
+  den = wave_sum(den);
+  float o[kE];
+#pragma unroll
+  for (int e = 0; e < kE; ++e) o[e] = 0.f;
+  for (int i = 0; i < np; ++i) {
+    const int64_t r = row0 + i * rstep;
+    const float wgt = fast_exp2(a.part_ml[2 * r] - M);
+    const float* src = a.part_acc + r * D + kE * lane;
+#pragma unroll
+    for (int e = 0; e < kE; ++e) o[e] += wgt * src[e];
+  }
+  const float inv = 1.f / den;
+  if constexpr (kE == 2)
+    *(uint32_t*)(O + orow) = pack_bf16x2(o[0] * inv, o[1] * inv);
+  else
+    O[orow] = f32_to_bf16_bits(o[0] * inv);
+}
+
+// Fixed-partition mode: grid (partitions, kv-head groups, requests).
+template <int D, int NW, bool kNT>
+__global__ __launch_bounds__(64 * NW) void decode_bf16_grid_kernel(DecodeArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int kvh = blockIdx.y * NW + (threadIdx.x >> 6);
   if (kvh >= a.num_kv_heads) return;  // whole wavefront; the kernel has no barrier
   const int s = blockIdx.z;
   const int part = blockIdx.x;
   const int P = a.partition_tokens;
-  const int G = a.group;
-  const int n = lane & 15;
-  const int g4 = lane >> 4;
-  const int h = kvh * G + n;
-  const bool head_ok = n < G;
-  const uint16_t* __restrict__ Q = (const uint16_t*)a.q;
-  const uint16_t* __restrict__ K = (const uint16_t*)a.k;
-  const uint16_t* __restrict__ V = (const uint16_t*)a.v;
-  uint16_t* __restrict__ O = (uint16_t*)a.out;
-  const int64_t qo_row = ((int64_t)s * a.num_q_heads + h) * D;
-
-  int L = a.context_lens[s];
-  L = min(L, a.max_context_len);
+  const int L = min(a.context_lens[s], a.max_context_len);
   if (L <= 0) {
-    if (part == 0 && head_ok) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int t = 0; t < kDL; ++t) O[qo_row + kDL * (4 * g4 + i) + t] = 0x7fc0;
+    const int n = lane & 15, g4 = lane >> 4;
+    if (part == 0 && n < a.group) {
+      uint16_t* O = (uint16_t*)a.out;
+      const int64_t qo_row = ((int64_t)s * a.num_q_heads + kvh * a.group + n) * D;
+      for (int i = 0; i < D / 4; ++i) O[qo_row + (D / 4) * g4 + i] = 0x7fc0;
     }
     return;
   }
@@ -88,151 +457,14 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_bf16_kernel(DecodeAr
   if (start >= L) return;
   const int end = min(start + P, L);
   const int nparts = (L + P - 1) / P;
-
-  u32x4 qb[kChunks];
-#pragma unroll
-  for (int c = 0; c < kChunks; ++c)
-    qb[c] = head_ok ? *(const u32x4*)(Q + qo_row + 32 * c + 8 * g4) : u32x4{0, 0, 0, 0};
-
-  f32x4 acc[kDL];
-#pragma unroll
-  for (int t = 0; t < kDL; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY;
-  float lsum = 0.f;
-  bool poisoned = false;
-
-  const int32_t* table = a.block_tables + (int64_t)s * a.max_blocks;
-  const int Hkv = a.num_kv_heads;
-  const int row_stride = Hkv * D;  // elements between consecutive tokens of a block
-  const int b_end = (end + 15) >> 4;
-
-  for (int b = start >> 4; b < b_end; b += 2) {
-    const bool two = b + 1 < b_end;
-    int32_t id0 = table_block(table, b * 16);
-    int32_t id1 = two ? table_block(table, (b + 1) * 16) : 0;
-    if (!block_ok(id0, a.num_blocks)) { poisoned = true; id0 = 0; }
-    if (!block_ok(id1, a.num_blocks)) { poisoned = true; id1 = 0; }
-
-    const uint16_t* k0 = K + kv_row(id0, n, kvh, Hkv, D) + 8 * g4;
-    const uint16_t* k1 = K + kv_row(id1, n, kvh, Hkv, D) + 8 * g4;
-    const uint16_t* v0 = V + kv_row(id0, 4 * g4, kvh, Hkv, D) + kDL * n;
-    const uint16_t* v1 = V + kv_row(id1, 4 * g4, kvh, Hkv, D) + kDL * n;
-    u32x4 ka0[kChunks], ka1[kChunks];
-    VRow vr[8];
-#pragma unroll
-    for (int c = 0; c < kChunks; ++c) ka0[c] = *(const u32x4*)(k0 + 32 * c);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) vr[j] = *(const VRow*)(v0 + j * row_stride);
-    if (two) {
-#pragma unroll
-      for (int c = 0; c < kChunks; ++c) ka1[c] = *(const u32x4*)(k1 + 32 * c);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) vr[4 + j] = *(const VRow*)(v1 + j * row_stride);
-    } else {
-#pragma unroll
-      for (int c = 0; c < kChunks; ++c) ka1[c] = u32x4{0, 0, 0, 0};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) vr[4 + j] = VRow{};
-    }
-
-    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int c = 0; c < kChunks; ++c) {
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka0[c]), as_bf16x8(qb[c]), s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka1[c]), as_bf16x8(qb[c]), s1, 0, 0, 0);
-    }
-    float sc[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sc[i] = s0[i] * a.scale_log2;
-      sc[4 + i] = s1[i] * a.scale_log2;
-    }
-    if ((b + 2) * 16 > end) {  // keys past the partition end: score -inf, V row 0
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int key = (b + (j >> 2)) * 16 + 4 * g4 + (j & 3);
-        if (key >= end) {
-          sc[j] = -INFINITY;
-          vr[j] = VRow{};
-        }
-      }
-    }
-    float tmax = sc[0];
-#pragma unroll
-    for (int j = 1; j < 8; ++j) tmax = fmaxf(tmax, sc[j]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const float m_new = fmaxf(m, tmax);
-    const float alpha = fast_exp2(m - m_new);
-    float p[8];
-    float psum = 0.f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      p[j] = fast_exp2(sc[j] - m_new);
-      psum += p[j];
-    }
-    lsum = lsum * alpha + psum;
-    m = m_new;
-    const u32x4 pb = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
-                      pack_bf16x2(p[6], p[7])};
-#pragma unroll
-    for (int t = 0; t < kDL; ++t) {
-      u32x4 va;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint32_t lo = vr[2 * u][t >> 1];
-        const uint32_t hi = vr[2 * u + 1][t >> 1];
-        va[u] = (t & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-      }
-      acc[t] *= alpha;
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va), as_bf16x8(pb), acc[t], 0, 0, 0);
-    }
-  }
-
-  lsum += __shfl_xor(lsum, 16, 64);
-  lsum += __shfl_xor(lsum, 32, 64);
-  if (poisoned) lsum = __builtin_nanf("");
-  if (!head_ok) return;
-  // lane (n, g4), acc[t][i] is head h at d = kDL * (4 g4 + i) + t
-  if (nparts == 1) {
-    const float inv = 1.f / lsum;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint16_t* dst = O + qo_row + kDL * (4 * g4 + i);
-      if constexpr (D == 128) {
-        u32x4 w;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) w[t] = pack_bf16x2(acc[2 * t][i] * inv, acc[2 * t + 1][i] * inv);
-        *(u32x4*)dst = w;
-      } else {
-        u32x2 w;
-#pragma unroll
-        for (int t = 0; t < 2; ++t) w[t] = pack_bf16x2(acc[2 * t][i] * inv, acc[2 * t + 1][i] * inv);
-        *(u32x2*)dst = w;
-      }
-    }
-  } else {
-    const int64_t pidx = ((int64_t)s * a.num_q_heads + h) * a.max_parts + part;
-    float* dst = a.part_acc + pidx * D;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int t4 = 0; t4 < kDL; t4 += 4) {
-        *(f32x4*)(dst + kDL * (4 * g4 + i) + t4) =
-            f32x4{acc[t4][i], acc[t4 + 1][i], acc[t4 + 2][i], acc[t4 + 3][i]};
-      }
-    }
-    if (g4 == 0) {
-      a.part_ml[2 * pidx] = m;
-      a.part_ml[2 * pidx + 1] = lsum;
-    }
-  }
+  decode_segment<D, kNT>(a, s, kvh, start >> 4, (end + 15) >> 4, end, nparts == 1,
+                         (int64_t)s * a.num_q_heads * a.max_parts + part, a.max_parts);
 }
 
-// fp32 pools: one wavefront per (request, kv head, partition); G <= 16 query heads.
+// fp32 pools, fixed-partition mode: one wavefront per (request, kv head, partition).
 template <int D>
 __global__ __launch_bounds__(64) void decode_f32_kernel(DecodeArgs a) {
-  constexpr int kE = D / 64;  // d values per lane
+  constexpr int kE = D / 64;  // dims per lane
   constexpr int kMaxG = 16;
   __shared__ float qs[kMaxG][D];
   __shared__ float ps[kMaxG][64];
@@ -249,8 +481,7 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(DecodeArgs a) {
   float* __restrict__ O = (float*)a.out;
   const int64_t head0 = (int64_t)s * a.num_q_heads + (int64_t)kvh * G;
 
-  int L = a.context_lens[s];
-  L = min(L, a.max_context_len);
+  const int L = min(a.context_lens[s], a.max_context_len);
   if (L <= 0) {
     if (part == 0)
       for (int g = 0; g < G; ++g)
@@ -352,16 +583,14 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(DecodeArgs a) {
   }
 }
 
-// Combine the partitions of every request longer than one partition.
-// One wavefront per (query head, request); lanes own D/64 consecutive d values.
+// Fixed-partition merge: one wavefront per (q head, request); lanes own D/64 dims.
 template <int D, bool kBf16>
 __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   constexpr int kE = D / 64;
   const int lane = threadIdx.x;
   const int h = blockIdx.x;
   const int s = blockIdx.y;
-  int L = a.context_lens[s];
-  L = min(L, a.max_context_len);
+  const int L = min(a.context_lens[s], a.max_context_len);
   if (L <= 0) return;
   const int P = a.partition_tokens;
   const int nparts = (L + P - 1) / P;
@@ -390,11 +619,10 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   const int64_t orow = ((int64_t)s * a.num_q_heads + h) * D + kE * lane;
   if constexpr (kBf16) {
     uint16_t* O = (uint16_t*)a.out;
-    if constexpr (kE == 2) {
+    if constexpr (kE == 2)
       *(uint32_t*)(O + orow) = pack_bf16x2(o[0] * inv, o[1] * inv);
-    } else {
+    else
       O[orow] = f32_to_bf16_bits(o[0] * inv);
-    }
   } else {
     float* O = (float*)a.out;
 #pragma unroll
@@ -402,26 +630,67 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   }
 }
 
+template <int D, int NW, bool kNT>
+void launch_grid(const DecodeArgs& a, hipStream_t stream) {
+  const int groups = (a.num_kv_heads + NW - 1) / NW;
+  hipLaunchKernelGGL((decode_bf16_grid_kernel<D, NW, kNT>), dim3(a.max_parts, groups, a.num_seqs),
+                     dim3(64 * NW), 0, stream, a);
+}
+
+template <int D, int NW>
+void launch_bf16_nw(const DecodeArgs& a, hipStream_t stream) {
+  if (a.num_workers > 0) {
+    const int groups = (a.num_kv_heads + NW - 1) / NW;
+    const size_t lds = sizeof(int32_t) * (size_t)(a.num_seqs + 1);
+    hipLaunchKernelGGL((decode_bf16_balanced_kernel<D, NW>), dim3(a.num_workers, groups),
+                       dim3(64 * NW), lds, stream, a);
+  } else if (a.nontemporal > 0) {
+    launch_grid<D, NW, true>(a, stream);
+  } else {
+    launch_grid<D, NW, false>(a, stream);
+  }
+}
+
 template <int D>
 hipError_t launch_decode_d(const DecodeArgs& a, bool bf16, hipStream_t stream) {
   if (bf16) {
-    dim3 grid(a.max_parts, (a.num_kv_heads + kDecodeWaves - 1) / kDecodeWaves, a.num_seqs);
-    hipLaunchKernelGGL(decode_bf16_kernel<D>, grid, dim3(64 * kDecodeWaves), 0, stream, a);
+    switch (decode_waves(a.num_kv_heads)) {
+      case 1: launch_bf16_nw<D, 1>(a, stream); break;
+      case 2: launch_bf16_nw<D, 2>(a, stream); break;
+      case 4: launch_bf16_nw<D, 4>(a, stream); break;
+      default: launch_bf16_nw<D, 8>(a, stream); break;
+    }
   } else {
-    dim3 grid(a.max_parts, a.num_kv_heads, a.num_seqs);
-    hipLaunchKernelGGL(decode_f32_kernel<D>, grid, dim3(64), 0, stream, a);
+    hipLaunchKernelGGL(decode_f32_kernel<D>, dim3(a.max_parts, a.num_kv_heads, a.num_seqs),
+                       dim3(64), 0, stream, a);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.max_parts <= 1) return e;
+  if (e != hipSuccess) return e;
   dim3 mgrid(a.num_q_heads, a.num_seqs);
-  if (bf16)
-    hipLaunchKernelGGL((decode_merge_kernel<D, true>), mgrid, dim3(64), 0, stream, a);
-  else
-    hipLaunchKernelGGL((decode_merge_kernel<D, false>), mgrid, dim3(64), 0, stream, a);
+  if (a.num_workers > 0) {
+    hipLaunchKernelGGL(decode_merge_balanced_kernel<D>, mgrid, dim3(64), 0, stream, a);
+  } else if (a.max_parts > 1) {
+    if (bf16)
+      hipLaunchKernelGGL((decode_merge_kernel<D, true>), mgrid, dim3(64), 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_merge_kernel<D, false>), mgrid, dim3(64), 0, stream, a);
+  }
   return hipGetLastError();
 }
 
 }  // namespace
+
+int decode_waves(int num_kv_heads) {
+  int nw = num_kv_heads >= 8 ? 8 : num_kv_heads >= 4 ? 4 : num_kv_heads >= 2 ? 2 : 1;
+  const char* e = getenv("PA_DECODE_WAVES");  // tuning override: 1, 2, 4 or 8
+  if (e != nullptr) {
+    const int v = atoi(e);
+    if (v == 1 || v == 2 || v == 4 || v == 8) nw = v;
+  }
+  return nw;
+}
+
+int decode_max_balanced_seqs() { return kMaxBalancedSeqs; }
 
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, bool bf16, hipStream_t stream) {
   if (head_dim == 128) return launch_decode_d<128>(a, bf16, stream);

@@ -106,24 +106,63 @@ int32_t choose_partition(const pa_cache_desc* d, int32_t num_seqs, int32_t max_c
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+int env_int(const char* name, int dflt) {
+  const char* e = std::getenv(name);
+  return e != nullptr ? std::atoi(e) : dflt;
+}
+
+// Balanced decode: enough workgroups for ~2048 wavefronts (8 per compute unit on
+// a 256-CU MI355X), each wavefront one kv head of one workgroup.
+int32_t balanced_workers(const pa_cache_desc* d) {
+  const int forced = env_int("PA_DECODE_WORKERS", 0);
+  if (forced > 0) return forced;
+  const int nw = pa::decode_waves(d->num_kv_heads);
+  const int groups = (d->num_kv_heads + nw - 1) / nw;
+  const int w = 2048 / (nw * groups);
+  return w > 0 ? w : 1;
+}
+
 struct DecodeLayout {
-  int32_t partition;
-  int32_t max_parts;
+  int32_t partition;  // fixed mode
+  int32_t max_parts;  // fixed mode
+  int32_t workers;    // balanced mode (0 = fixed mode)
   size_t acc_bytes;
+  size_t ml_bytes;
   size_t total;
 };
 
 DecodeLayout decode_layout(const pa_cache_desc* d, int32_t num_seqs, int32_t max_context_len,
                            int32_t partition_tokens) {
   DecodeLayout l{};
-  l.partition = partition_tokens > 0 ? partition_tokens
-                                     : choose_partition(d, num_seqs, max_context_len);
-  l.max_parts = (int32_t)(((int64_t)max_context_len + l.partition - 1) / l.partition);
-  if (l.max_parts <= 1) return l;
-  const size_t rows = (size_t)num_seqs * d->num_q_heads * l.max_parts;
+  size_t rows = 0;
+  if (d->dtype == PA_BF16 && partition_tokens == 0 && num_seqs <= pa::decode_max_balanced_seqs()) {
+    l.workers = balanced_workers(d);
+    rows = ((size_t)num_seqs + l.workers) * d->num_q_heads;
+  } else {
+    l.partition = partition_tokens > 0 ? partition_tokens
+                                       : choose_partition(d, num_seqs, max_context_len);
+    l.max_parts = (int32_t)(((int64_t)max_context_len + l.partition - 1) / l.partition);
+    if (l.max_parts <= 1) return l;
+    rows = (size_t)num_seqs * d->num_q_heads * l.max_parts;
+  }
   l.acc_bytes = align256(rows * d->head_dim * sizeof(float));
-  l.total = l.acc_bytes + align256(rows * 2 * sizeof(float));
+  l.ml_bytes = align256(rows * 2 * sizeof(float));
+  l.total = l.acc_bytes + l.ml_bytes;
+  if (l.workers > 0) l.total += align256(((size_t)num_seqs + 1) * sizeof(int32_t));
   return l;
+}
+
+// Non-temporal K/V loads: -1 lets the balanced kernel decide from the total
+// attended blocks; the fixed-partition kernel streams when no block can be read
+// twice and the pool is far larger than the 256 MiB last-level cache.
+int32_t nontemporal_mode(const pa_cache_desc* d, int32_t num_seqs, int32_t max_context_len,
+                         bool balanced) {
+  const int forced = env_int("PA_DECODE_NT", -1);
+  if (forced >= 0) return forced != 0;
+  if (balanced) return -1;
+  const int64_t pool_tokens = d->num_blocks * PA_BLOCK_SIZE;
+  const int64_t pool_bytes = 2 * pool_tokens * d->num_kv_heads * d->head_dim * elem_bytes(d->dtype);
+  return (int64_t)num_seqs * max_context_len <= pool_tokens && pool_bytes >= ((int64_t)1 << 30);
 }
 
 }  // namespace
@@ -238,6 +277,7 @@ int pa_decode(const pa_cache_desc* desc, void* out, const void* q, const void* k
   a.context_lens = context_lens;
   a.part_acc = lay.total ? (float*)workspace : nullptr;
   a.part_ml = lay.total ? (float*)((char*)workspace + lay.acc_bytes) : nullptr;
+  a.cum_blocks = lay.workers ? (int32_t*)((char*)workspace + lay.acc_bytes + lay.ml_bytes) : nullptr;
   a.num_blocks = desc->num_blocks;
   a.max_blocks = max_blocks_per_seq;
   a.num_seqs = num_seqs;
@@ -247,6 +287,8 @@ int pa_decode(const pa_cache_desc* desc, void* out, const void* q, const void* k
   a.group = desc->num_q_heads / desc->num_kv_heads;
   a.partition_tokens = lay.partition;
   a.max_parts = lay.max_parts;
+  a.num_workers = lay.workers;
+  a.nontemporal = nontemporal_mode(desc, num_seqs, max_context_len, lay.workers > 0);
   a.scale_log2 = scale * pa::kLog2e;
   return hip_status(pa::launch_decode(a, desc->head_dim, desc->dtype == PA_BF16, as_stream(stream)),
                     "decode launch");

@@ -89,8 +89,11 @@ struct DecodeArgs {
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t group;
-  int32_t partition_tokens;
-  int32_t max_parts;
+  int32_t partition_tokens;  // fixed-partition mode: keys per partition
+  int32_t max_parts;         // fixed-partition mode: partitions of the longest request
+  int32_t num_workers;       // balanced mode: workgroups along the block axis (0 = fixed mode)
+  int32_t nontemporal;       // stream K/V past the caches: 1 yes, 0 no, -1 kernel decides
+  int32_t* cum_blocks;       // balanced mode: [S+1] prefix sums of blocks per request
   float scale_log2;  // scale * log2(e)
 };
 
@@ -117,6 +120,10 @@ hipError_t launch_write_kv(const void* key, const void* value, void* k_cache, vo
                            const int32_t* slots, int64_t num_tokens, int row_bytes,
                            int64_t num_slots, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, bool bf16, hipStream_t stream);
+// kv heads handled by one decode workgroup (one wavefront each)
+int decode_waves(int num_kv_heads);
+// most requests the balanced decode mode accepts (block prefix sums live in LDS)
+int decode_max_balanced_seqs();
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int group, hipStream_t stream);
 hipError_t launch_gather_kv(void* dst_k, void* dst_v, const void* k_cache, const void* v_cache,
                             const int32_t* block_tables, int32_t max_blocks,

@@ -122,3 +122,31 @@ def test_empty_batch_and_bad_length():
     torch.cuda.synchronize()
     o = as64(out)
     assert np.all(np.isnan(o[1])) and np.all(np.isfinite(o[[0, 2]]))
+
+
+@pytest.mark.parametrize("workers", [1, 3, 7, 64, 1000])
+def test_balanced_worker_counts(workers, monkeypatch):
+    """Any split of the block axis over workers gives the same result (segments cut anywhere)."""
+    monkeypatch.setenv("PA_DECODE_WORKERS", str(workers))
+    w = workloads.c2_decode_batch(seed=8, num_seqs=12, len_lo=1, len_hi=1500)
+    check(w, 0, f"workers {workers}")
+
+
+@pytest.mark.parametrize("nt", ["0", "1"])
+def test_load_flavours(nt, monkeypatch):
+    monkeypatch.setenv("PA_DECODE_NT", nt)
+    check(workloads.c3_prefix_shared(seed=12, num_seqs=20), 0, f"nontemporal={nt}")
+
+
+def test_balanced_relabelling_and_sharing_bit_identical():
+    w = workloads.c3_prefix_shared(seed=13, num_seqs=6, prefix_tokens=64, tail_lo=1, tail_hi=300,
+                                   Hq=8, Hkv=2, D=128)
+    d, k, v = gpu_pools(w)
+    base = host_bits(run_decode(w, d, k, v))
+    perm = torch.from_numpy(np.random.default_rng(13).permutation(w.spec.num_blocks)).cuda()
+    k2, v2 = torch.empty_like(k), torch.empty_like(v)
+    k2[perm], v2[perm] = k, v
+    bt = w.decode.block_tables.copy()
+    pn = perm.cpu().numpy()
+    bt[bt >= 0] = pn[bt[bt >= 0]]
+    assert np.array_equal(base, host_bits(run_decode(w, d, k2, v2, tables=bt)))
