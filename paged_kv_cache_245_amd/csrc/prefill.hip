@@ -9,13 +9,11 @@
 // paged, like virtual memory").
 //
 // This is a dense contraction (QK^T and PV), so it runs on bf16 MFMA.
-// Workgroup = 4 wavefronts = 128 "packed" query rows of one (request, kv head):
+// Workgroup = 8 wavefronts = 256 "packed" query rows of one (request, kv head):
 // row r is (position r / G, query head kvh*G + r % G), so all G heads sharing a
 // kv head share every K/V tile (grouped-query attention). Keys go in tiles of
-// 64 (four 16-token blocks), staged in LDS:
-//   Ks [64 keys][D]   row-major; 16-byte chunks XOR-swizzled by row,
-//   Vt [D][64 keys]   transposed; each 8-key run is one 16-byte chunk, the
-//                     chunks XOR-swizzled by row, keys ordered to match P.
+// 64 (four 16-token blocks), staged in double-buffered LDS, K and V both
+// row-major [64 keys][D] with their 16-byte chunks XOR-swizzled by row.
 // Staging: wavefronts 0-1 copy K rows (8 x 16 B per lane); wavefronts 2-3 load
 // an 8-key x 8-dim patch of V per lane, transpose it in registers and store
 // eight 16-byte runs. The next tile is loaded into registers while the current
@@ -26,7 +24,8 @@
 //     8(i/4) + 4 half + i%4 (i = 0..15) of row col, so a row's softmax needs
 //     one cross-lane step.
 //   O^T[32 dims x 32 rows] += V^T . P^T (4 MFMAs of 16 keys per 32 dims):
-//     P^T is the lane's own probabilities (bf16), V^T one 16-byte LDS read.
+//     P^T is the lane's own probabilities (bf16); V^T comes from two transposed
+//     8-byte LDS reads whose key order matches P.
 // fp32 online softmax in log2 units (one FMA and one v_exp_f32 per score), fp32
 // accumulation; the running max moves only when a tile exceeds it by 2^8, so the
 // output is rescaled rarely (exact: numerator and denominator share the max).
@@ -41,35 +40,41 @@
 namespace pa {
 namespace {
 
-constexpr int kRows = 128;  // packed query rows per workgroup
-constexpr int kBN = 64;     // keys per tile
-constexpr int kThreads = 256;
+constexpr int kWaves = 8;             // wavefronts per workgroup, 32 query rows each
+constexpr int kRows = 32 * kWaves;    // packed query rows per workgroup
+constexpr int kBN = 64;               // keys per tile
+constexpr int kThreads = 64 * kWaves;
 
-// LDS slot (in 16-byte chunks) of chunk `ch` of K row `row` (kCh chunks per row).
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+// Physical 16-byte chunk of logical chunk `ch` in row `row` of a staged tile.
+// K rows: the row's low 4 bits (16-lane K reads hit 16 distinct chunks).
+// V rows: 2 x (row & 3), so the 4 consecutive keys of a transposed read fall on
+// 8 distinct chunks.
 template <int kCh>
-__device__ __forceinline__ int k_slot(int row, int ch) {
-  if constexpr (kCh == 16) return row * 16 + (ch ^ (row & 15));
-  else return row * kCh + (ch ^ ((row >> 1) & (kCh - 1)));
+__device__ __forceinline__ int k_phys(int row, int ch) {
+  if constexpr (kCh == 16) return ch ^ (row & 15);
+  else return ch ^ ((row >> 1) & 7);
 }
-
-// LDS slot of chunk `ch` (keys 8 ch .. 8 ch + 7, permuted) of transposed-V row d.
-__device__ __forceinline__ int v_slot(int d, int ch) { return d * 8 + (ch ^ ((d >> 1) & 7)); }
+__device__ __forceinline__ int v_phys(int row, int ch) { return ch ^ (2 * (row & 3)); }
 
 template <int D, int G>
-__global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a) {
   static_assert(D == 64 || D == 128, "head_dim");
-  constexpr int kPos = kRows / G;        // query positions per workgroup
-  constexpr int kKCh = D / 8;            // 16-byte chunks per key row
-  constexpr int kKRowsPerThr = kBN * kKCh / 128;
-  constexpr int kKRowStep = 128 / kKCh;  // rows between one K-lane's loads
-  constexpr float kRescale = 8.f;        // log2 headroom before the running max is moved
-  // two stages of K and transposed V
-  __shared__ u32x4 Ks[2][kBN * kKCh];
-  __shared__ u32x4 Vt[2][D * 8];
+  constexpr int kPos = kRows / G;            // query positions per workgroup
+  constexpr int kCh = D / 8;                 // 16-byte chunks per key row
+  constexpr int kTileCh = kBN * kCh;         // chunks per staged tile of K (or V)
+  constexpr int kInstr = 2 * kTileCh / kThreads;  // 16-byte pieces per lane and tile
+  constexpr float kRescale = 8.f;            // log2 headroom before the running max is moved
+  static_assert(kInstr * kThreads == 2 * kTileCh && (kInstr * 64) % kCh == 0, "staging");
+  // two stages of K and V, both row-major [64 keys][D]
+  __shared__ u32x4 Ks[2][kTileCh];
+  __shared__ u32x4 Vs[2][kTileCh];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int Hkv = a.num_kv_heads;
   const int kvh = blockIdx.x % Hkv;
   const int s = blockIdx.x / Hkv;
@@ -111,69 +116,69 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
   const int64_t block_elems = (int64_t)kBlock * Hkv * D;
   const int row_elems = Hkv * D;
 
-  // staging roles (wavefront-uniform): threads 0..127 copy K, 128..255 transpose V
-  const bool k_role = tid < 128;
-  const int st = tid & 127;
-  const int kc = st % kKCh, kr = st / kKCh;  // K: chunk kc of rows kr + kKRowStep j
-  // V: dims 8 vd .. 8 vd + 7 of keys 16 vu + 8 (j/4) + 4 vh + j%4 (first D threads)
-  const int vd = st % (D / 8), vuh = st / (D / 8), vu = vuh >> 1, vh = vuh & 1;
-  const bool v_active = st < D;
-  // per-lane element offsets inside a block (kv head kvh), fixed for the whole kernel
-  const int k_off = kvh * D + 8 * kc;
-  const int v_off = kvh * D + 8 * vd;
-  u32x4 stage[8];
-
+  // Staging: wavefronts 0-3 copy K, 4-7 copy V; wavefront w takes block w % 4 of
+  // the tile. Piece i of lane l is LDS chunk slot ((w%4)*kInstr + i)*64 + l, i.e.
+  // row slot/kCh, physical chunk slot%kCh, which holds logical chunk
+  // k_phys/v_phys(row, physical). Pieces go to registers at the top of a tile and
+  // are stored to the other LDS stage at its end.
+  const int sblk = wave & 3;          // block of the tile this wavefront copies
+  const bool s_is_v = wave >= 4;      // wavefront-uniform
+  int src_off[kInstr];                // element offsets inside a block (tile-independent)
+#pragma unroll
+  for (int i = 0; i < kInstr; ++i) {
+    const int slot = (sblk * kInstr + i) * 64 + lane;
+    const int row = slot / kCh;
+    const int ch = s_is_v ? v_phys(row, slot % kCh) : k_phys<kCh>(row, slot % kCh);
+    src_off[i] = (row & 15) * row_elems + kvh * D + 8 * ch;
+  }
+  u32x4 sreg[kInstr];
+  // block ids this wavefront copies, 64 tiles at a time: lane j holds tile id_tile0 + j
+  int id_tile0 = 0;
+  auto fetch_ids = [&]() {
+    const int blk = 4 * (id_tile0 + lane) + sblk;
+    return blk < nblocks ? table[blk] : 0;
+  };
+  int32_t idv = fetch_ids();
   auto stage_load = [&](int t) {
     const int key0 = t * kBN;
-    const uint16_t* kbase[kBN / 16];
-    const uint16_t* vbase[kBN / 16];
-#pragma unroll
-    for (int q = 0; q < kBN / 16; ++q) {
-      const int blk = (key0 >> 4) + q;
-      int32_t id = blk < nblocks ? table[blk] : 0;
-      if (!block_ok(id, a.num_blocks)) { poisoned = true; id = 0; }
-      kbase[q] = a.k + (int64_t)id * block_elems;
-      vbase[q] = a.v + (int64_t)id * block_elems;
+    if (t - id_tile0 >= 64) {  // tiles are staged in order
+      id_tile0 += 64;
+      idv = fetch_ids();
     }
-    const bool full = key0 + kBN <= L;  // uniform: no key of the tile is past the context
-    if (k_role) {
+    int32_t id = __builtin_amdgcn_readlane(idv, t - id_tile0);
+    if (!block_ok(id, a.num_blocks)) { poisoned = true; id = 0; }
+    const uint16_t* src = (s_is_v ? a.v : a.k) + (int64_t)id * block_elems;
+    const bool full = key0 + 16 * (sblk + 1) <= L;  // uniform: the whole block is in range
 #pragma unroll
-      for (int j = 0; j < kKRowsPerThr; ++j) {
-        const int row = kr + kKRowStep * j;
-        const uint16_t* src = kbase[row >> 4] + (row & 15) * row_elems + k_off;
-        stage[j] = (full || key0 + row < L) ? *(const u32x4*)src : u32x4{0, 0, 0, 0};
-      }
-    } else if (v_active) {
-      const uint16_t* vb = vbase[0];
-#pragma unroll
-      for (int q = 1; q < kBN / 16; ++q) vb = vu == q ? vbase[q] : vb;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int tok = 8 * (j >> 2) + 4 * vh + (j & 3);  // token inside block vu
-        const uint16_t* src = vb + tok * row_elems + v_off;
-        stage[j] = (full || key0 + 16 * vu + tok < L) ? *(const u32x4*)src : u32x4{0, 0, 0, 0};
-      }
+    for (int i = 0; i < kInstr; ++i) {
+      const int row = ((sblk * kInstr + i) * 64 + lane) / kCh;
+      const bool in = full || key0 + row < L;  // past the context: zeros
+      sreg[i] = in ? *(const u32x4*)(src + src_off[i]) : u32x4{0, 0, 0, 0};
     }
   };
   auto stage_store = [&](int buf) {
-    if (k_role) {
+    u32x4* dst = s_is_v ? &Vs[buf][0] : &Ks[buf][0];
 #pragma unroll
-      for (int j = 0; j < kKRowsPerThr; ++j) Ks[buf][k_slot<kKCh>(kr + kKRowStep * j, kc)] = stage[j];
-    } else if (v_active) {
-      // transpose 8 keys x 8 dims: run e holds dim 8 vd + e of the 8 keys
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        u32x4 run;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const uint32_t lo = stage[2 * u][e >> 1];
-          const uint32_t hi = stage[2 * u + 1][e >> 1];
-          run[u] = (e & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-        }
-        Vt[buf][v_slot(8 * vd + e, 2 * vu + vh)] = run;
-      }
-    }
+    for (int i = 0; i < kInstr; ++i) dst[(sblk * kInstr + i) * 64 + lane] = sreg[i];
   };
+
+  // Per-lane LDS byte addresses of the MFMA operands in stage 0 (stage 1 is +kTileCh*16).
+  //   K (A of S^T): row 32 kb + col, logical chunk 2c + half  -> one per c, kb by offset
+  //   V (A of O^T, transposed read): lane (i = lane%16, group g = lane/16) supplies row
+  //   16u + 8rr + 4 half + i/4 and dims 32 dt + 16 (g&1) + 4 (i%4)   -> one per dt
+  uint32_t k_addr[D / 16], v_addr[D / 32];
+  const uint32_t ks0 = (uint32_t)(uintptr_t)&Ks[0][0], vs0 = (uint32_t)(uintptr_t)&Vs[0][0];
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) k_addr[c] = ks0 + 16u * (col * kCh + k_phys<kCh>(col, 2 * c + half));
+  {
+    const int i = lane & 15, g = lane >> 4;
+    const int vrow = 4 * half + (i >> 2);  // + 16u + 8rr, which leave row & 3 unchanged
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      const int dim = 32 * dt + 16 * (g & 1) + 4 * (i & 3);
+      v_addr[dt] = vs0 + 16u * (vrow * kCh + v_phys(vrow, dim >> 3)) + 2u * (dim & 7);
+    }
+  }
 
   f32x16 o[D / 32];
 #pragma unroll
@@ -191,21 +196,32 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
   for (int t = 0; t < n_tiles; ++t) {
     const int buf = t & 1;
     const int key0 = t * kBN;
+    const uint32_t koff = buf * kTileCh * 16u, voff = buf * kTileCh * 16u;
     f32x16 sacc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
+    {
+      typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
+      u32x4 ka[2][2];  // operands of chunk c (ping) and c+1 (pong)
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c) {
+      for (int kb = 0; kb < 2; ++kb)
+        ka[0][kb] = *(lds_u32x4*)(uintptr_t)(k_addr[0] + koff + kb * 32 * kCh * 16);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const u32x4 ka = Ks[buf][k_slot<kKCh>(32 * kb + col, 2 * c + half)];
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka), as_bf16x8(qb[c]), sacc[kb], 0, 0, 0);
+      for (int c = 0; c < D / 16; ++c) {
+        if (c + 1 < D / 16) {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+            ka[(c + 1) & 1][kb] = *(lds_u32x4*)(uintptr_t)(k_addr[c + 1] + koff + kb * 32 * kCh * 16);
+        }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[c & 1][kb]), as_bf16x8(qb[c]), sacc[kb], 0, 0, 0);
       }
     }
     // scores are transformed in place: raw -> masked -> probability
-    if (key0 + kBN - 1 > first_limit) {  // tile crosses the causal diagonal of some row
+    if (key0 + kBN - 1 > first_limit) {  // tile crosses the causal diagonal (or the end)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -253,11 +269,15 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
     for (int u = 0; u < 4; ++u) {
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
-        const u32x4 va = Vt[buf][v_slot(32 * dt + col, 2 * u + half)];
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va), as_bf16x8(pb[u]), o[dt], 0, 0, 0);
+        // keys 16u + 4 half + 0..3 (rr = 0) and 16u + 8 + 4 half + 0..3 (rr = 1)
+        const uint32_t base = v_addr[dt] + voff + u * 16 * kCh * 16;
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(uintptr_t)base);
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(uintptr_t)(base + 8 * kCh * 16));
+        const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, as_bf16x8(pb[u]), o[dt], 0, 0, 0);
       }
     }
-    // tile t+1 goes to the other buffer, last read by tile t-1 (before the previous barrier)
+    // tile t+1 goes to the other stage, last read by tile t-1 (before the last barrier)
     if (t + 1 < n_tiles) stage_store(buf ^ 1);
     __syncthreads();
     if (t + 2 < n_tiles) stage_load(t + 2);
