@@ -7,6 +7,7 @@ from .paged_attention import (  # noqa: F401
     empty_pool,
     slot_location,
     write_kv,
+    copy_blocks,
     blocks_for,
     gather_logical,
     kv_head_of,

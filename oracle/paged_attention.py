@@ -92,6 +92,28 @@ def write_kv(k_pool, v_pool, key, value, slot_mapping) -> None:
         v_pool[b, o] = value[i]
 
 
+def copy_blocks(k_pool, v_pool, block_pairs) -> None:
+    """Duplicate whole blocks in place, K and V: block dst becomes a bit copy of block src.
+
+    This is the copy-on-write step for forked sequences that share blocks until
+    one writes into a shared block (aitrending, "The 1960s Operating System Trick
+    That Makes vLLM 4x Faster", Technical Details). Destinations must be distinct
+    and no block may be both a source and a destination in one call.
+    """
+    pairs = np.asarray(block_pairs, dtype=np.int64).reshape(-1, 2)
+    src, dst = pairs[:, 0].tolist(), pairs[:, 1].tolist()
+    if len(set(dst)) != len(dst):
+        raise ValueError("a block is a destination twice")
+    if set(dst) & set(src):
+        raise ValueError("a block is both a source and a destination")
+    nb = k_pool.shape[0]
+    for a, b in zip(src, dst):
+        if not (0 <= a < nb and 0 <= b < nb):
+            raise IndexError("block pair outside the pool")
+        k_pool[b] = k_pool[a]
+        v_pool[b] = v_pool[a]
+
+
 def blocks_for(num_tokens: int) -> int:
     """Blocks covering num_tokens tokens: ceil(num_tokens / 16)."""
     return (int(num_tokens) + BLOCK_SIZE - 1) // BLOCK_SIZE

@@ -17,6 +17,7 @@ from ._lib import (  # noqa: F401
     pa_bench_copy,
     pa_bench_flush,
     pa_bench_read,
+    pa_copy_blocks,
     pa_decode,
     pa_decode_partition_tokens,
     pa_decode_workspace_size,

@@ -20,7 +20,7 @@ PA_BF16 = 1
 BLOCK_SIZE = 16
 
 EXPORTED = ("pa_write_kv", "pa_decode_partition_tokens", "pa_decode_workspace_size", "pa_decode",
-            "pa_prefill_chunk", "pa_gather_kv", "pa_strerror", "pa_last_error_detail",
+            "pa_prefill_chunk", "pa_copy_blocks", "pa_gather_kv", "pa_strerror", "pa_last_error_detail",
             "pa_version", "pa_bench_copy", "pa_bench_read", "pa_bench_flush")
 
 
@@ -68,6 +68,7 @@ def load():
         "pa_decode_workspace_size": (SZ, [D, I32, I32, I32]),
         "pa_decode": (ctypes.c_int, [D, P, P, P, P, P, I32, P, I32, I32, F, I32, P, SZ, P]),
         "pa_prefill_chunk": (ctypes.c_int, [D, P, P, P, P, P, P, P, I32, I32, I32, I32, I32, F, P]),
+        "pa_copy_blocks": (ctypes.c_int, [D, P, P, P, I64, P]),
         "pa_gather_kv": (ctypes.c_int, [D, P, P, P, P, P, I32, P, I32, I32, P]),
         "pa_strerror": (ctypes.c_char_p, [ctypes.c_int]),
         "pa_last_error_detail": (ctypes.c_char_p, []),
@@ -188,6 +189,19 @@ def pa_prefill_chunk(desc, out, q, k_cache, v_cache, query_start_loc, seq_lens, 
                                  int(max_query_len), int(max_seq_len), float(scale),
                                  _stream(stream, q))
     _check(st, "pa_prefill_chunk")
+
+
+def pa_copy_blocks(desc, k_cache, v_cache, block_pairs, stream=None):
+    """block_pairs int32 [n, 2]: (source block, destination block) per row."""
+    dt = torch_dtype(desc)
+    _need(k_cache, dt, "k_cache")
+    _need(v_cache, dt, "v_cache")
+    _need(block_pairs, torch.int32, "block_pairs", 2)
+    if block_pairs.shape[1] != 2:
+        raise ValueError("block_pairs must be [n, 2]")
+    st = load().pa_copy_blocks(ctypes.byref(desc), _ptr(k_cache), _ptr(v_cache), _ptr(block_pairs),
+                               block_pairs.shape[0], _stream(stream, k_cache))
+    _check(st, "pa_copy_blocks")
 
 
 def pa_gather_kv(desc, dst_k, dst_v, k_cache, v_cache, block_tables, context_lens,

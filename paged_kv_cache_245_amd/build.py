@@ -20,8 +20,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpa.so")
 
-SOURCES = ["pa_api.hip", "write_kv.hip", "decode.hip", "prefill.hip", "gather_kv.hip",
-           "bench_kernels.hip"]
+SOURCES = ["pa_api.hip", "write_kv.hip", "decode.hip", "prefill.hip", "copy_blocks.hip",
+           "gather_kv.hip", "bench_kernels.hip"]
 ARCH = "gfx950"
 # Packed fp32 VALU forms are kept out of the device code on purpose.
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",

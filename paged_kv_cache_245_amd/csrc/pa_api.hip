@@ -21,12 +21,9 @@ int fail(int status, const std::string& what) {
   return status;
 }
 
-bool check_mode() {
-  static const bool on = [] {
-    const char* e = std::getenv("PA_CHECK");
-    return e != nullptr && e[0] == '1';
-  }();
-  return on;
+bool check_mode() {  // read on every call, so a process can switch it on and off
+  const char* e = std::getenv("PA_CHECK");
+  return e != nullptr && e[0] == '1';
 }
 
 int elem_bytes(int32_t dtype) { return dtype == PA_BF16 ? 2 : 4; }
@@ -355,6 +352,39 @@ int pa_prefill_chunk(const pa_cache_desc* desc, void* out, const void* q, const 
   return hip_status(pa::launch_prefill(a, desc->head_dim, desc->num_q_heads / desc->num_kv_heads,
                                        as_stream(stream)),
                     "prefill launch");
+}
+
+int pa_copy_blocks(const pa_cache_desc* desc, void* k_cache, void* v_cache,
+                   const int32_t* block_pairs, int64_t num_pairs, void* stream) {
+  int st = validate_desc(desc);
+  if (st != PA_OK) return st;
+  if (num_pairs < 0) return fail(PA_ERR_INVALID_ARG, "num_pairs is negative");
+  if (num_pairs == 0) return PA_OK;
+  if (num_pairs > INT32_MAX) return fail(PA_ERR_UNSUPPORTED, "too many pairs");
+  if (!k_cache || !v_cache || !block_pairs) return fail(PA_ERR_INVALID_ARG, "null pointer argument");
+  if (check_mode()) {
+    if (hipStreamSynchronize(as_stream(stream)) != hipSuccess)
+      return fail(PA_ERR_HIP, "stream synchronize failed");
+    std::vector<int32_t> pairs;
+    if (!fetch(pairs, block_pairs, (size_t)num_pairs * 2)) return fail(PA_ERR_HIP, "copy of pairs failed");
+    std::unordered_set<int32_t> dsts, srcs;
+    for (int64_t i = 0; i < num_pairs; ++i) {
+      const int32_t src = pairs[2 * i], dst = pairs[2 * i + 1];
+      if (src < 0 || src >= desc->num_blocks || dst < 0 || dst >= desc->num_blocks)
+        return fail(PA_ERR_RANGE, "pair " + std::to_string(i) + " is outside the pool");
+      if (!dsts.insert(dst).second)
+        return fail(PA_ERR_RANGE, "block " + std::to_string(dst) + " is a destination twice");
+      srcs.insert(src);
+    }
+    for (int32_t d : dsts)
+      if (srcs.count(d))
+        return fail(PA_ERR_RANGE, "block " + std::to_string(d) + " is both a source and a destination");
+  }
+  const int64_t block_bytes =
+      (int64_t)PA_BLOCK_SIZE * desc->num_kv_heads * desc->head_dim * elem_bytes(desc->dtype);
+  return hip_status(pa::launch_copy_blocks(k_cache, v_cache, block_pairs, num_pairs, block_bytes,
+                                           desc->num_blocks, as_stream(stream)),
+                    "copy_blocks launch");
 }
 
 int pa_gather_kv(const pa_cache_desc* desc, void* dst_k, void* dst_v, const void* k_cache,

@@ -130,6 +130,8 @@ hipError_t launch_gather_kv(void* dst_k, void* dst_v, const void* k_cache, const
                             const int32_t* context_lens, int32_t num_seqs,
                             int32_t max_context_len, int row_bytes, int num_kv_heads,
                             int64_t num_blocks, hipStream_t stream);
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int64_t num_pairs,
+                              int64_t block_bytes, int64_t num_blocks, hipStream_t stream);
 hipError_t launch_bench_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
 hipError_t launch_bench_read(const void* src, size_t bytes, float* sink, hipStream_t stream);
 hipError_t launch_bench_flush(void* buf, size_t bytes, hipStream_t stream);

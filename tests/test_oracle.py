@@ -248,6 +248,47 @@ def pin_split_kv_identity():
         assert np.max(np.abs(got - ref)) <= 1e-12, part
 
 
+def pin_copy_blocks():
+    """A copied block equals its source bit for bit; nothing else changes; bad pairs raise."""
+    k = oracle.empty_pool(6, 2, 4, "bf16", 0x7FC0)
+    rng = np.random.default_rng(3)
+    k[:] = rng.integers(0, 1 << 16, size=k.shape, dtype=np.uint16)
+    v = k ^ np.uint16(0x5555)
+    k0, v0 = k.copy(), v.copy()
+    pa_oracle.copy_blocks(k, v, [[1, 4], [1, 5], [2, 0]])
+    assert np.array_equal(k[4], k0[1]) and np.array_equal(k[5], k0[1]) and np.array_equal(k[0], k0[2])
+    assert np.array_equal(v[4], v0[1]) and np.array_equal(v[0], v0[2])
+    assert np.array_equal(k[[1, 2, 3]], k0[[1, 2, 3]])
+    for bad in ([[1, 3], [2, 3]], [[1, 3], [3, 4]], [[1, 6]]):
+        with pytest.raises((ValueError, IndexError)):
+            pa_oracle.copy_blocks(k.copy(), v.copy(), bad)
+
+
+def pin_copy_on_write_fork():
+    """Fork a request, copy its last shared block, write the fork's next token into the copy:
+    the parent's output is unchanged and the fork attends parent tokens + its new token."""
+    w = custom_decode(43, [37], Hq=4, Hkv=2, D=8, dtype="bf16")
+    k, v = oracle_pools(w)
+    d = w.decode
+    parent = oracle.decode(d.q, k, v, d.block_tables, d.context_lens, "bf16")
+    spare = [b for b in range(k.shape[0]) if b not in set(d.block_tables[0, :3].tolist())][0]
+    fork = d.block_tables[:1].copy()
+    last = int(fork[0, 2])  # tokens 32..36 live in the third block
+    pa_oracle.copy_blocks(k, v, [[last, spare]])
+    fork[0, 2] = spare
+    new_k = (np.arange(2 * 8, dtype=np.uint16).reshape(1, 2, 8) + 0x3F00).astype(np.uint16)
+    new_v = new_k ^ np.uint16(0x0101)
+    oracle.write_kv(k, v, new_k, new_v, np.array([spare * 16 + 5], np.int32))  # token 37
+    again = oracle.decode(d.q, k, v, d.block_tables, d.context_lens, "bf16")
+    assert np.array_equal(again, parent)
+    K, V = logical64(w, 0)
+    K = np.concatenate([K, values64(new_k, "bf16")])
+    V = np.concatenate([V, values64(new_v, "bf16")])
+    got = oracle.decode(d.q, k, v, fork, np.array([38], np.int32), "bf16")
+    ref = sdpa_rows(values64(d.q, "bf16"), K, V, causal=False)
+    assert np.max(np.abs(got[0] - ref[0])) <= 1e-12
+
+
 def pin_empty_context_rejected():
     k = oracle.empty_pool(2, 1, 4, "f32", 0)
     with pytest.raises(ValueError):
@@ -260,7 +301,7 @@ ALL_PINS = [
     pin_context_one, pin_zero_query_mean, pin_one_hot, pin_two_key_closed_form,
     pin_softmax_weights, pin_permutation_invariance, pin_prefix_sharing,
     pin_gqa_equals_repeated_mha, pin_chunk_is_rows_of_full, pin_decode_is_one_row_chunk,
-    pin_split_kv_identity, pin_empty_context_rejected,
+    pin_split_kv_identity, pin_empty_context_rejected, pin_copy_blocks, pin_copy_on_write_fork,
 ]
 
 
@@ -314,6 +355,10 @@ MISTAKES = {
         lambda q, k, v, lim, sc: pa_oracle.softmax_weights(
             np.where(np.arange(k.shape[0])[None, :] > np.asarray(lim)[:, None], -np.inf,
                      sc * (q @ v.T))) @ k),
+    "block copy reversed": (
+        "copy_blocks",
+        lambda kp, vp, pairs: [kp.__setitem__(int(a), kp[int(b)]) or vp.__setitem__(int(a), vp[int(b)])
+                               for a, b in np.asarray(pairs).reshape(-1, 2)] and None),
     "table read backwards": (
         "gather_logical",
         lambda pool, row, L: pool[np.asarray(row[:(L + 15) // 16])[::-1]].reshape(
