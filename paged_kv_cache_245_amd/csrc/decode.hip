@@ -385,6 +385,50 @@ __device__ __forceinline__ int worker_of(int64_t b, int64_t T, int W) {
 }
 
 // Balanced mode merge: one wavefront per (q head, request); lanes own D/64 dims.
+// Merge of split-KV partials (m, l, acc) of one (request, q head): partial i is
+// row row0 + i * rstep of the workspace. Returns o = sum_i 2^(m_i - M) acc_i and
+// den = sum_i 2^(m_i - M) l_i for M = max_i m_i; the caller divides.
+// Partials are read eight at a time, all loads of a batch issued before any use,
+// and folded into a running (M, den, o) rescaled to the batch maximum.
+template <int D>
+__device__ __forceinline__ void fold_partials(const DecodeArgs& a, int64_t row0, int64_t rstep, int np,
+                                              int lane, float (&o)[D / 64], float& den) {
+  constexpr int kE = D / 64;
+  constexpr int kBatch = 8;
+  float M = -INFINITY;
+  den = 0.f;
+#pragma unroll
+  for (int e = 0; e < kE; ++e) o[e] = 0.f;
+  for (int i0 = 0; i0 < np; i0 += kBatch) {
+    float mi[kBatch], li[kBatch], ai[kBatch][kE];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const bool in = i0 + j < np;
+      const int64_t r = row0 + (int64_t)(in ? i0 + j : 0) * rstep;
+      mi[j] = in ? a.part_ml[2 * r] : -INFINITY;
+      li[j] = in ? a.part_ml[2 * r + 1] : 0.f;
+      const float* src = a.part_acc + r * D + kE * lane;
+#pragma unroll
+      for (int e = 0; e < kE; ++e) ai[j][e] = in ? src[e] : 0.f;
+    }
+    float mb = M;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) mb = fmaxf(mb, mi[j]);
+    const float alpha = fast_exp2(M - mb);  // 0 on the first batch
+    den *= alpha;
+#pragma unroll
+    for (int e = 0; e < kE; ++e) o[e] *= alpha;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const float wgt = fast_exp2(mi[j] - mb);  // 0 for padding
+      den += wgt * li[j];
+#pragma unroll
+      for (int e = 0; e < kE; ++e) o[e] += wgt * ai[j][e];
+    }
+    M = mb;
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(64) void decode_merge_balanced_kernel(DecodeArgs a) {
   constexpr int kE = D / 64;
@@ -407,26 +451,8 @@ __global__ __launch_bounds__(64) void decode_merge_balanced_kernel(DecodeArgs a)
   const int np = w1 - w0 + 1;
   // partial of worker w0 + i for this (request, head) is row (s + w0 + i) * Hq + h
   const int64_t row0 = ((int64_t)s + w0) * a.num_q_heads + h;
-  const int64_t rstep = a.num_q_heads;
-  float M = -INFINITY;
-  for (int i = lane; i < np; i += 64) M = fmaxf(M, a.part_ml[2 * (row0 + i * rstep)]);
-  M = wave_max(M);
-  float den = 0.f;
-  for (int i = lane; i < np; i += 64) {
-    const int64_t r = row0 + i * rstep;
-    den += fast_exp2(a.part_ml[2 * r] - M) * a.part_ml[2 * r + 1];
-  }
-  den = wave_sum(den);
-  float o[kE];
-#pragma unroll
-  for (int e = 0; e < kE; ++e) o[e] = 0.f;
-  for (int i = 0; i < np; ++i) {
-    const int64_t r = row0 + i * rstep;
-    const float wgt = fast_exp2(a.part_ml[2 * r] - M);
-    const float* src = a.part_acc + r * D + kE * lane;
-#pragma unroll
-    for (int e = 0; e < kE; ++e) o[e] += wgt * src[e];
-  }
+  float o[kE], den;
+  fold_partials<D>(a, row0, a.num_q_heads, np, lane, o, den);
   const float inv = 1.f / den;
   if constexpr (kE == 2)
     *(uint32_t*)(O + orow) = pack_bf16x2(o[0] * inv, o[1] * inv);
@@ -596,25 +622,8 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   const int nparts = (L + P - 1) / P;
   if (nparts <= 1) return;
   const int64_t base = ((int64_t)s * a.num_q_heads + h) * a.max_parts;
-  const float* ml = a.part_ml + 2 * base;
-  const float* pacc = a.part_acc + base * D;
-
-  float M = -INFINITY;
-  for (int p = lane; p < nparts; p += 64) M = fmaxf(M, ml[2 * p]);
-  M = wave_max(M);
-  float den = 0.f;
-  for (int p = lane; p < nparts; p += 64) den += fast_exp2(ml[2 * p] - M) * ml[2 * p + 1];
-  den = wave_sum(den);
-
-  float o[kE];
-#pragma unroll
-  for (int e = 0; e < kE; ++e) o[e] = 0.f;
-  for (int p = 0; p < nparts; ++p) {
-    const float w = fast_exp2(ml[2 * p] - M);
-    const float* src = pacc + (int64_t)p * D + kE * lane;
-#pragma unroll
-    for (int e = 0; e < kE; ++e) o[e] += w * src[e];
-  }
+  float o[kE], den;
+  fold_partials<D>(a, base, 1, nparts, lane, o, den);
   const float inv = 1.f / den;
   const int64_t orow = ((int64_t)s * a.num_q_heads + h) * D + kE * lane;
   if constexpr (kBf16) {
