@@ -1,9 +1,12 @@
-"""Build libpa.so (the gfx950 HIP kernels and their C ABI) in-tree with hipcc.
+"""Build the package's two shared libraries in-tree.
 
     python -m paged_kv_cache_245_amd.build [-v]
 
-Compiles every csrc/*.hip to an object under _build/ (in parallel) and links
-paged_kv_cache_245_amd/libpa.so. Always recompiles.
+libpa.so: every csrc/*.hip (the gfx950 HIP kernels and their C ABI, include/pa.h)
+compiled with hipcc to objects under _build/ (in parallel) and linked.
+libpa_host.so: the host-side block pool and scheduler (include/pa_pool.h,
+include/pa_sched.h), plain C++ built with g++; it needs no GPU and no ROCm.
+Always recompiles.
 """
 from __future__ import annotations
 
@@ -22,6 +25,8 @@ LIB = os.path.join(PKG, "libpa.so")
 
 SOURCES = ["pa_api.hip", "write_kv.hip", "decode.hip", "prefill.hip", "copy_blocks.hip",
            "gather_kv.hip", "bench_kernels.hip"]
+HOST_SOURCES = ["block_pool.cpp"]
+HOST_LIB = os.path.join(PKG, "libpa_host.so")
 ARCH = "gfx950"
 # Packed fp32 VALU forms are kept out of the device code on purpose.
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
@@ -49,7 +54,20 @@ def _run(cmd, verbose):
         print("\n".join(lines), flush=True)
 
 
+def build_host(verbose: bool = False) -> str:
+    """libpa_host.so with the host C++ compiler."""
+    cxx = os.environ.get("CXX") or shutil.which("g++") or shutil.which("c++")
+    if cxx is None:
+        raise RuntimeError("no host C++ compiler found for libpa_host.so")
+    tmp = HOST_LIB + ".tmp"
+    _run([cxx, "-O2", "-std=c++17", "-fPIC", "-shared", "-Wall", "-Wextra", "-I", INCLUDE,
+          *[os.path.join(CSRC, s) for s in HOST_SOURCES], "-o", tmp], verbose)
+    os.replace(tmp, HOST_LIB)
+    return HOST_LIB
+
+
 def build(verbose: bool = False, jobs: int | None = None) -> str:
+    build_host(verbose)
     os.makedirs(BUILD, exist_ok=True)
     cc = hipcc()
     objs = []
