@@ -1,5 +1,5 @@
-"""CPU oracle for paged-KV attention (fp64, paged_attention) and a plain model of the host
-block pool (block_pool). TEST INFRASTRUCTURE: imported only by the tests, the smoke check and
+"""CPU oracle for paged-KV attention (fp64, paged_attention) and plain models of the host
+block pool (block_pool) and step scheduler (scheduler). TEST INFRASTRUCTURE: imported only by the tests, the smoke check and
 the benchmark's CPU baseline; never by the HIP library, the host library or their bindings."""
 from . import paged_attention  # noqa: F401
 from .paged_attention import (  # noqa: F401

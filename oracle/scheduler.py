@@ -1,0 +1,165 @@
+"""Plain Python model of the continuous-batching step scheduler.
+
+TEST INFRASTRUCTURE. Only the tests may import this module; the library and its
+binding never do. It drives the block-pool model of oracle/block_pool.py.
+
+Rules and where they come from (arcyou teardown of vLLM paged attention,
+sections "Continuous batching: rebuild the batch every step" and "What happens
+when the blocks run out"):
+  * There are no prefill and decode phases: a request is (tokens computed,
+    tokens known), and each step hands out a token budget.
+  * Running requests are served first, then waiting ones are admitted until the
+    budget runs out; a long prompt is split over steps (chunked prefill).
+  * When the pool cannot grow a request, the newest running request is preempted
+    (FCFS), or the lowest-priority, latest-arrival one (priority scheduling); its
+    blocks are freed, its computed count reset to 0, and it goes back to the head
+    of the waiting queue to be recomputed.
+  * A finished request frees its blocks at once.
+
+Readings where the pages are silent (the same as the library's): no admission
+in a step that preempted; without chunked prefill, admission stops at the first
+waiting request whose remaining tokens exceed the budget left; under priority
+scheduling the waiting queue is kept in (priority, arrival) order and a victim
+already scheduled in the step is taken out of it; a request finishes on its
+max_new_tokens-th generated token, which is not appended; the batch lists the
+requests given more than one token first, then the one-token ones.
+"""
+from __future__ import annotations
+
+from .block_pool import BlockPoolModel
+
+FCFS, PRIORITY = 0, 1
+
+
+class SchedulerModel:
+    def __init__(self, pool: BlockPoolModel, max_num_batched_tokens: int, max_num_seqs: int,
+                 policy: int = FCFS, chunked_prefill: bool = True):
+        self.pool = pool
+        self.budget = max_num_batched_tokens
+        self.max_seqs = max_num_seqs
+        self.policy = policy
+        self.chunked = chunked_prefill
+        self.info = {}       # id -> dict(max_new, priority, arrival, produced)
+        self.waiting = []    # head first
+        self.running = []    # start order
+        self.plan = []       # (id, start, count), batch order
+        self.finished = []
+        self.preemptions = 0
+        self.arrivals = 0
+
+    # ---------------------------------------------------------------- rules
+    def rank(self, rid):
+        i = self.info[rid]
+        return (i["priority"], i["arrival"])
+
+    def enqueue(self, rid, preempted):
+        if self.policy == PRIORITY:
+            k = 0
+            while k < len(self.waiting) and self.rank(self.waiting[k]) <= self.rank(rid):
+                k += 1
+            self.waiting.insert(k, rid)
+        elif preempted:
+            self.waiting.insert(0, rid)
+        else:
+            self.waiting.append(rid)
+
+    def victim(self):
+        if self.policy == PRIORITY:
+            return max(self.running, key=self.rank)
+        return self.running[-1]
+
+    # ---------------------------------------------------------------- calls
+    def add_request(self, rid, prompt, max_new_tokens, priority=0, salt=0):
+        self.pool.add_request(rid, prompt, salt)
+        self.info[rid] = dict(max_new=max_new_tokens, priority=priority, arrival=self.arrivals, produced=0)
+        self.arrivals += 1
+        self.enqueue(rid, False)
+
+    def schedule(self):
+        order = []
+        budget = self.budget
+        preempted = False
+        i = 0
+        while i < len(self.running) and budget > 0:
+            rid = self.running[i]
+            r = self.pool.reqs[rid]
+            start = r.computed
+            n = min(len(r.tokens) - start, budget)
+            if n <= 0:
+                i += 1
+                continue
+            gone = False
+            while self.pool.allocate_slots(rid, n) is None:
+                v = self.victim()
+                vi = self.running.index(v)
+                self.running.remove(v)
+                for item in order:
+                    if item[0] == v:
+                        budget += item[2]
+                        order.remove(item)
+                        break
+                self.pool.free_request(v, keep=True)
+                self.enqueue(v, True)
+                self.preemptions += 1
+                preempted = True
+                if v == rid:
+                    gone = True
+                    break
+                if vi < i:
+                    i -= 1
+            if gone:
+                continue
+            order.append((rid, start, n))
+            budget -= n
+            i += 1
+        while (not preempted and self.waiting and budget > 0
+               and len(self.running) < self.max_seqs):
+            rid = self.waiting[0]
+            hit = self.pool.prefix_hit_tokens(rid)
+            lacking = len(self.pool.reqs[rid].tokens) - hit
+            if not self.chunked and lacking > budget:
+                break
+            n = min(lacking, budget)
+            if self.pool.allocate_slots(rid, n) is None:
+                break
+            self.waiting.pop(0)
+            self.running.append(rid)
+            order.append((rid, hit, n))
+            budget -= n
+        self.plan = [x for x in order if x[2] > 1] + [x for x in order if x[2] == 1]
+        return list(self.plan)
+
+    def batch(self, pad_block=0):
+        """query_start_loc, seq_lens, block tables, slot mapping, positions of the plan."""
+        qsl = [0]
+        seq, tables, slots, pos = [], [], [], []
+        width = max([len(self.pool.reqs[rid].blocks) for rid, _, _ in self.plan] + [1])
+        for rid, start, n in self.plan:
+            if n > 1:
+                qsl.append(qsl[-1] + n)
+            seq.append(start + n)
+            t = self.pool.block_table(rid)
+            tables.append(t + [pad_block] * (width - len(t)))
+            slots += self.pool.slot_mapping(rid, start, n)
+            pos += list(range(start, start + n))
+        return qsl, seq, tables, slots, pos
+
+    def update(self, sampled):
+        done = 0
+        for i, (rid, start, n) in enumerate(self.plan):
+            r = self.pool.reqs[rid]
+            self.pool.commit(rid, start + n)
+            if start + n < len(r.tokens):
+                continue
+            info = self.info[rid]
+            info["produced"] += 1
+            if info["produced"] >= info["max_new"]:
+                self.pool.free_request(rid)
+                self.running.remove(rid)
+                del self.info[rid]
+                self.finished.append(rid)
+                done += 1
+            else:
+                self.pool.append_tokens(rid, [sampled[i]])
+        self.plan = []
+        return done

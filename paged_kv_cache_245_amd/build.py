@@ -25,7 +25,7 @@ LIB = os.path.join(PKG, "libpa.so")
 
 SOURCES = ["pa_api.hip", "write_kv.hip", "decode.hip", "prefill.hip", "copy_blocks.hip",
            "gather_kv.hip", "bench_kernels.hip"]
-HOST_SOURCES = ["block_pool.cpp"]
+HOST_SOURCES = ["block_pool.cpp", "sched.cpp"]
 HOST_LIB = os.path.join(PKG, "libpa_host.so")
 ARCH = "gfx950"
 # Packed fp32 VALU forms are kept out of the device code on purpose.

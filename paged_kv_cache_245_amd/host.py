@@ -1,7 +1,9 @@
-"""ctypes binding of libpa_host.so: the host-side block pool of include/pa_pool.h.
+"""ctypes binding of libpa_host.so: the host-side block pool (include/pa_pool.h) and
+step scheduler (include/pa_sched.h).
 
-Argument marshalling only; every rule of the pool runs in the C++ library. The
-calls keep the C names without the pa_pool_ prefix, as methods of BlockPool.
+Argument marshalling only; every rule of the pool and the scheduler runs in the
+C++ library. The calls keep the C names without the pa_pool_ / pa_sched_
+prefix, as methods of BlockPool and Scheduler.
 """
 from __future__ import annotations
 
@@ -187,3 +189,152 @@ class BlockPool:
 
     def block_hash(self, req_id: int, i: int) -> int:
         return self._lib.pa_pool_block_hash(self._p, req_id, i)
+
+
+# ----------------------------------------------------------------------------- scheduler
+SCHED_FCFS = 0
+SCHED_PRIORITY = 1
+
+SCHED_EXPORTED = ("pa_sched_create", "pa_sched_destroy", "pa_sched_add_request", "pa_sched_schedule",
+                  "pa_sched_plan", "pa_sched_plan_tokens", "pa_sched_plan_prefills",
+                  "pa_sched_plan_max_blocks", "pa_sched_batch", "pa_sched_update",
+                  "pa_sched_num_waiting", "pa_sched_num_running", "pa_sched_num_preemptions",
+                  "pa_sched_take_finished", "pa_sched_last_error")
+
+
+class SchedConfig(ctypes.Structure):
+    _fields_ = [("max_num_batched_tokens", ctypes.c_int32), ("max_num_seqs", ctypes.c_int32),
+                ("policy", ctypes.c_int32), ("chunked_prefill", ctypes.c_int32)]
+
+
+def _load_sched(lib):
+    if getattr(lib, "_sched_ready", False):
+        return lib
+    P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    PI32, PI64 = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
+    sig = {
+        "pa_sched_create": (P, [P, ctypes.POINTER(SchedConfig)]),
+        "pa_sched_destroy": (None, [P]),
+        "pa_sched_add_request": (ctypes.c_int, [P, I64, PI32, I64, I32, I32, I64]),
+        "pa_sched_schedule": (I64, [P]),
+        "pa_sched_plan": (ctypes.c_int, [P, PI64, PI32, PI32]),
+        "pa_sched_plan_tokens": (I64, [P]),
+        "pa_sched_plan_prefills": (I64, [P]),
+        "pa_sched_plan_max_blocks": (I32, [P]),
+        "pa_sched_batch": (ctypes.c_int, [P, PI32, PI32, PI32, I32, I32, PI32, PI32]),
+        "pa_sched_update": (I64, [P, PI32]),
+        "pa_sched_num_waiting": (I64, [P]),
+        "pa_sched_num_running": (I64, [P]),
+        "pa_sched_num_preemptions": (I64, [P]),
+        "pa_sched_take_finished": (I64, [P, PI64, I64]),
+        "pa_sched_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    lib._sched_ready = True
+    return lib
+
+
+class SchedError(RuntimeError):
+    def __init__(self, status: int, call: str):
+        detail = load_host().pa_sched_last_error().decode()
+        super().__init__(f"{call}: status {status}{': ' + detail if detail else ''}")
+        self.status = status
+
+
+class StepBatch:
+    """One step's plan and device-call metadata (numpy int32 arrays, batch order)."""
+
+    def __init__(self, req_ids, starts, counts, num_prefills, query_start_loc, seq_lens,
+                 block_tables, slot_mapping, positions):
+        self.req_ids, self.starts, self.counts = req_ids, starts, counts
+        self.num_prefills = num_prefills
+        self.query_start_loc, self.seq_lens = query_start_loc, seq_lens
+        self.block_tables, self.slot_mapping, self.positions = block_tables, slot_mapping, positions
+
+    @property
+    def num_seqs(self) -> int:
+        return len(self.req_ids)
+
+    @property
+    def num_tokens(self) -> int:
+        return int(self.counts.sum())
+
+
+class Scheduler:
+    """Owns one pa_scheduler over a BlockPool; methods mirror pa_sched_* (include/pa_sched.h)."""
+
+    def __init__(self, pool: BlockPool, max_num_batched_tokens: int, max_num_seqs: int,
+                 policy: int = SCHED_FCFS, chunked_prefill: bool = True):
+        self._lib = _load_sched(load_host())
+        self.pool = pool  # kept alive as long as the scheduler
+        cfg = SchedConfig(max_num_batched_tokens, max_num_seqs, policy, int(bool(chunked_prefill)))
+        self._s = self._lib.pa_sched_create(pool.handle, ctypes.byref(cfg))
+        if not self._s:
+            raise SchedError(-1, "pa_sched_create")
+
+    def close(self) -> None:
+        if self._s:
+            self._lib.pa_sched_destroy(self._s)
+            self._s = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def _check(self, st, call):
+        if st < 0:
+            raise SchedError(st, call)
+        return st
+
+    def add_request(self, req_id, prompt, max_new_tokens, priority=0, cache_salt=0) -> None:
+        t = _i32(prompt)
+        self._check(self._lib.pa_sched_add_request(self._s, req_id, _p32(t), t.size, max_new_tokens,
+                                                   priority, cache_salt), "pa_sched_add_request")
+
+    def schedule(self, pad_block: int = 0) -> StepBatch:
+        n = self._check(self._lib.pa_sched_schedule(self._s), "pa_sched_schedule")
+        ids = np.zeros(max(n, 1), dtype=np.int64)
+        starts = np.zeros(max(n, 1), dtype=np.int32)
+        counts = np.zeros(max(n, 1), dtype=np.int32)
+        self._check(self._lib.pa_sched_plan(self._s, ids.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                            _p32(starts), _p32(counts)), "pa_sched_plan")
+        ids, starts, counts = ids[:n], starts[:n], counts[:n]
+        p = self._check(self._lib.pa_sched_plan_prefills(self._s), "pa_sched_plan_prefills")
+        tok = int(counts.sum())
+        mb = max(self._lib.pa_sched_plan_max_blocks(self._s), 1)
+        qsl = np.zeros(p + 1, dtype=np.int32)
+        seq = np.zeros(max(n, 1), dtype=np.int32)
+        tables = np.zeros((max(n, 1), mb), dtype=np.int32)
+        slots = np.zeros(max(tok, 1), dtype=np.int32)
+        pos = np.zeros(max(tok, 1), dtype=np.int32)
+        self._check(self._lib.pa_sched_batch(self._s, _p32(qsl), _p32(seq), _p32(tables), mb, pad_block,
+                                             _p32(slots), _p32(pos)), "pa_sched_batch")
+        return StepBatch(ids, starts, counts, p, qsl, seq[:n], tables[:n], slots[:tok], pos[:tok])
+
+    def update(self, sampled) -> int:
+        t = _i32(sampled) if len(sampled) else np.zeros(1, dtype=np.int32)
+        return self._check(self._lib.pa_sched_update(self._s, _p32(t)), "pa_sched_update")
+
+    def num_waiting(self) -> int:
+        return self._lib.pa_sched_num_waiting(self._s)
+
+    def num_running(self) -> int:
+        return self._lib.pa_sched_num_running(self._s)
+
+    def num_preemptions(self) -> int:
+        return self._lib.pa_sched_num_preemptions(self._s)
+
+    def take_finished(self):
+        buf = np.zeros(4096, dtype=np.int64)
+        out = []
+        while True:
+            n = self._lib.pa_sched_take_finished(self._s, buf.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                                 buf.size)
+            out += buf[:n].tolist()
+            if n < buf.size:
+                return out

@@ -1,0 +1,222 @@
+"""Pins of the scheduler model (oracle/scheduler.py) against what the pages state.
+
+Each pin checks one stated behaviour of continuous batching (arcyou teardown of
+vLLM paged attention, "Continuous batching: rebuild the batch every step" and
+"What happens when the blocks run out") on a small hand-built case, plus an
+end-to-end run in which K/V are simulated as token ids: every request always
+reads back its own tokens, every request ends with exactly its number of
+generated tokens, and the budget is never exceeded. Planted mistakes in the
+model must each be caught by at least one pin.
+"""
+import random
+
+import pytest
+
+from oracle import block_pool as bp
+from oracle import scheduler as sm
+
+B = bp.BLOCK
+
+
+def make(num_blocks, budget, max_seqs=64, policy=sm.FCFS, chunked=True, prefix=True):
+    return sm.SchedulerModel(bp.BlockPoolModel(num_blocks, prefix), budget, max_seqs, policy, chunked)
+
+
+def step(s, dev=None, rng=None, produced=None):
+    plan = s.schedule()
+    if produced is not None:
+        for rid, start, n in plan:
+            if start + n == len(s.pool.reqs[rid].tokens):
+                produced[rid] = produced.get(rid, 0) + 1
+    if dev is not None:
+        _, _, _, slots, pos = s.batch()
+        k = 0
+        for rid, start, n in plan:
+            toks = s.pool.reqs[rid].tokens
+            for j in range(n):
+                dev[slots[k]] = toks[pos[k]]
+                k += 1
+    sampled = [(rng.randint(0, 99) if rng else 7) for _ in plan]
+    s.update(sampled)
+    return plan
+
+
+def readback_ok(s, dev):
+    for rid, r in s.pool.reqs.items():
+        got = [dev.get(r.blocks[p // B] * B + p % B) for p in range(r.computed)]
+        if got != r.tokens[:r.computed]:
+            return False
+    return True
+
+
+# ----------------------------------------------------------------------------- pins
+def pin_chunked_prefill_splits_a_long_prompt():
+    s = make(64, 32)
+    s.add_request(1, list(range(100)), 3)
+    assert [step(s)[0][2] for _ in range(4)] == [32, 32, 32, 4]
+    assert step(s) == [(1, 100, 1)]  # then one token per step
+
+
+def pin_steps_mix_prompts_and_generation():
+    s = make(64, 64)
+    s.add_request(1, list(range(20)), 5)
+    step(s)
+    s.add_request(2, list(range(200, 240)), 5)
+    plan = step(s)
+    assert sorted(n for _, _, n in plan) == [1, 40]
+    assert plan[0][0] == 2  # multi-token requests lead the batch
+
+
+def pin_running_served_before_waiting():
+    s = make(64, 40)
+    s.add_request(1, list(range(70)), 2)
+    step(s)                                  # 40 of 70
+    s.add_request(2, list(range(100, 110)), 2)
+    plan = step(s)
+    assert plan[0] == (1, 40, 30) and (2, 0, 10) in plan
+
+
+def pin_budget_is_never_exceeded():
+    rng = random.Random(3)
+    s = make(40, 24)
+    for i in range(12):
+        s.add_request(i, [rng.randint(0, 9) for _ in range(rng.randint(1, 60))], rng.randint(1, 6))
+    for _ in range(200):
+        plan = step(s, rng=rng)
+        assert sum(n for _, _, n in plan) <= 24
+
+
+def pin_preemption_takes_the_newest_and_requeues_it_first():
+    s = make(6, 64)
+    s.add_request(1, list(range(40)), 30)    # 3 blocks
+    s.add_request(2, list(range(100, 140)), 30)  # 3 blocks: the pool is full
+    step(s)
+    s.add_request(3, [5, 5], 1)
+    for _ in range(30):                      # request 1 needs a 4th block at position 48
+        step(s)
+        if s.preemptions:
+            break
+    assert s.preemptions == 1
+    assert s.running == [1] and s.waiting == [2, 3] and s.pool.reqs[2].computed == 0
+    assert s.pool.prefix_hit_tokens(2) >= 32  # its prefix survived in the pool
+
+
+def pin_priority_preempts_lowest_priority_latest_arrival():
+    s = make(6, 64, policy=sm.PRIORITY)
+    s.add_request(1, list(range(40)), 30, priority=5)
+    s.add_request(2, list(range(100, 140)), 30, priority=0)
+    step(s)
+    for _ in range(30):
+        step(s)
+        if s.preemptions:
+            break
+    assert s.preemptions == 1 and s.running == [2] and s.waiting == [1]
+
+
+def pin_finished_requests_release_their_blocks():
+    s = make(8, 64)
+    s.add_request(1, list(range(30)), 1)
+    step(s)
+    assert s.finished == [1] and len(s.pool.free) == 8 and s.running == []
+
+
+def pin_no_admission_beyond_max_seqs():
+    s = make(64, 64, max_seqs=2)
+    for i in range(4):
+        s.add_request(i, [i] * 5, 3)
+    plan = step(s)
+    assert [rid for rid, _, _ in plan] == [0, 1] and s.waiting == [2, 3]
+
+
+def pin_without_chunking_a_prompt_waits_for_room():
+    s = make(64, 32, chunked=False)
+    s.add_request(1, list(range(20)), 4)
+    s.add_request(2, list(range(50)), 4)
+    plan = step(s)
+    assert [rid for rid, _, _ in plan] == [1] and s.waiting == [2]
+
+
+def pin_trace_completes_and_reads_back():
+    for seed in range(12):
+        rng = random.Random(seed)
+        s = make(rng.choice([8, 12, 40]), rng.choice([16, 48]), max_seqs=rng.choice([2, 8]),
+                 policy=rng.choice([sm.FCFS, sm.PRIORITY]))
+        dev, produced, max_new = {}, {}, {}
+        shared = [rng.randint(0, 9) for _ in range(32)]
+        for i in range(10):
+            prompt = (shared if rng.random() < 0.5 else []) + [rng.randint(0, 9) for _ in range(rng.randint(1, 40))]
+            max_new[i] = rng.randint(1, 8)
+            s.add_request(i, prompt, max_new[i], priority=rng.randint(0, 2))
+        for _ in range(2000):
+            step(s, dev, rng, produced)
+            assert readback_ok(s, dev)
+            if not s.running and not s.waiting:
+                break
+        assert sorted(s.finished) == list(range(10))
+        assert produced == max_new
+
+
+ALL_PINS = [pin_chunked_prefill_splits_a_long_prompt, pin_steps_mix_prompts_and_generation,
+            pin_running_served_before_waiting, pin_budget_is_never_exceeded,
+            pin_preemption_takes_the_newest_and_requeues_it_first,
+            pin_priority_preempts_lowest_priority_latest_arrival,
+            pin_finished_requests_release_their_blocks, pin_no_admission_beyond_max_seqs,
+            pin_without_chunking_a_prompt_waits_for_room, pin_trace_completes_and_reads_back]
+
+
+@pytest.mark.parametrize("pin", ALL_PINS, ids=lambda f: f.__name__)
+def test_pin(pin):
+    pin()
+
+
+MISTAKES = {
+    "preempt the oldest": ("victim", lambda self: self.running[0]),
+    "preempted request to the tail": ("enqueue", lambda self, rid, pre: self.waiting.append(rid)),
+    "priority ignored when preempting": ("rank", lambda self, rid: (0, self.info[rid]["arrival"])),
+}
+
+
+def _plan_order_decodes_first(self):
+    plan = _orig_schedule(self)
+    self.plan = [x for x in plan if x[2] == 1] + [x for x in plan if x[2] > 1]
+    return list(self.plan)
+
+
+def _no_chunking(self):
+    self.chunked = False
+    saved, self.budget = self.budget, 10 ** 9
+    try:
+        return _orig_schedule(self)
+    finally:
+        self.budget = saved
+
+
+def _keep_finished_blocks(self, sampled):
+    free = self.pool.free_request
+    self.pool.free_request = lambda rid, keep=False: None if not keep else free(rid, keep)
+    try:
+        return _orig_update(self, sampled)
+    finally:
+        self.pool.free_request = free
+
+
+_orig_schedule = sm.SchedulerModel.schedule
+_orig_update = sm.SchedulerModel.update
+MISTAKES.update({
+    "decodes lead the batch": ("schedule", _plan_order_decodes_first),
+    "whole prompts ignore the budget": ("schedule", _no_chunking),
+    "finished requests keep their blocks": ("update", _keep_finished_blocks),
+})
+
+
+@pytest.mark.parametrize("name", sorted(MISTAKES))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    attr, wrong = MISTAKES[name]
+    monkeypatch.setattr(sm.SchedulerModel, attr, wrong)
+    failed = []
+    for pin in ALL_PINS:
+        try:
+            pin()
+        except Exception:  # noqa: BLE001 - any failure counts
+            failed.append(pin.__name__)
+    assert failed, f"no pin noticed the planted mistake {name!r}"
