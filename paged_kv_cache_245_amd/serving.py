@@ -1,0 +1,89 @@
+"""One continuous-batching step on the GPU, from a host scheduler's batch.
+
+A step (arcyou teardown of vLLM paged attention, "Continuous batching: rebuild
+the batch every step") mixes prompt chunks and single generated tokens. Given
+the batch that libpa_host.so's scheduler planned (host.Scheduler.schedule), this
+module moves its metadata to the GPU in one copy and issues, on one stream:
+pa_copy_blocks for pending copy-on-write pairs, pa_write_kv for every new
+token's K/V, pa_prefill_chunk for the requests given more than one token, and
+pa_decode for the ones given exactly one. Marshalling and sequencing only; the
+work runs in libpa.so's kernels.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import _lib as pa
+
+
+class StepRunner:
+    """Device buffers for the steps of one pool: metadata staging and the decode workspace.
+
+    Metadata goes through two pinned host buffers used in turn; before one is
+    refilled, the copy that last read it is waited for, so the host can plan the
+    next step while the GPU runs the previous one.
+    """
+
+    def __init__(self, desc, k_cache, v_cache, scale, max_seqs, max_tokens, max_blocks_per_seq,
+                 device="cuda"):
+        self.desc, self.k, self.v, self.scale = desc, k_cache, v_cache, float(scale)
+        self.max_seqs, self.max_tokens, self.max_blocks = max_seqs, max_tokens, max_blocks_per_seq
+        self.device = torch.device(device)
+        # room for one step's metadata (int32): qsl | seq_lens | tables | slots
+        self.n_meta = (max_seqs + 1) + max_seqs + max_seqs * max_blocks_per_seq + max_tokens
+        self.host = [torch.empty(self.n_meta, dtype=torch.int32, pin_memory=True) for _ in range(2)]
+        self.done = [None, None]
+        self.turn = 0
+        self.meta = torch.empty(self.n_meta, dtype=torch.int32, device=self.device)
+        self.ws = pa.decode_workspace(desc, max_seqs, max_blocks_per_seq * 16, 0, self.device)
+        self.ws_bytes = 0 if self.ws is None else self.ws.numel()
+
+    def run(self, batch, q, key, value, out, copies=()):
+        """q/out [N, Hq, D], key/value [N, Hkv, D]: the step's new tokens in batch order."""
+        S, N, P = batch.num_seqs, batch.num_tokens, batch.num_prefills
+        if S == 0:
+            return
+        mb = batch.block_tables.shape[1]
+        if S > self.max_seqs or N > self.max_tokens or mb > self.max_blocks:
+            raise ValueError("step larger than the buffers of this StepRunner")
+        stream = torch.cuda.current_stream(self.device)
+        if copies:
+            pairs = torch.tensor(np.asarray(copies, dtype=np.int32).reshape(-1, 2), device=self.device)
+            pa.pa_copy_blocks(self.desc, self.k, self.v, pairs)
+
+        # pack the metadata (qsl | seq_lens | tables | slots) into the next pinned buffer,
+        # then one host-to-device copy of the used length
+        buf = self.host[self.turn]
+        if self.done[self.turn] is not None:
+            self.done[self.turn].synchronize()
+        h = buf.numpy()
+        o_seq = P + 1
+        o_tab = o_seq + S
+        o_slot = o_tab + S * mb
+        end = o_slot + N
+        h[:o_seq] = batch.query_start_loc
+        h[o_seq:o_tab] = batch.seq_lens
+        h[o_tab:o_slot] = batch.block_tables.reshape(-1)
+        h[o_slot:end] = batch.slot_mapping
+        self.meta[:end].copy_(buf[:end], non_blocking=True)
+        ev = torch.cuda.Event()
+        ev.record(stream)
+        self.done[self.turn] = ev
+        self.turn ^= 1
+
+        qsl = self.meta[:o_seq]
+        seq = self.meta[o_seq:o_tab]
+        tables = self.meta[o_tab:o_slot].view(S, mb)
+        slots = self.meta[o_slot:end]
+        pa.pa_write_kv(self.desc, key[:N], value[:N], self.k, self.v, slots)
+        n_pf = int(batch.query_start_loc[-1])
+        if P:
+            pa.pa_prefill_chunk(self.desc, out[:n_pf], q[:n_pf], self.k, self.v, qsl, seq[:P], tables[:P],
+                                int(batch.counts[:P].max()), int(batch.seq_lens[:P].max()), self.scale)
+        if S > P:
+            need = pa.pa_decode_workspace_size(self.desc, S - P, int(batch.seq_lens[P:].max()))
+            if need > self.ws_bytes:
+                raise ValueError("decode workspace too small for this step")
+            pa.pa_decode(self.desc, out[n_pf:N], q[n_pf:N], self.k, self.v, tables[P:], seq[P:],
+                         int(batch.seq_lens[P:].max()), self.scale, self.ws)
