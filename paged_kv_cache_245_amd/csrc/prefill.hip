@@ -13,19 +13,19 @@
 // row r is (position r / G, query head kvh*G + r % G), so all G heads sharing a
 // kv head share every K/V tile (grouped-query attention). Keys go in tiles of
 // 64 (four 16-token blocks), staged in double-buffered LDS, K and V both
-// row-major [64 keys][D] with their 16-byte chunks XOR-swizzled by row.
-// Staging: wavefronts 0-1 copy K rows (8 x 16 B per lane); wavefronts 2-3 load
-// an 8-key x 8-dim patch of V per lane, transpose it in registers and store
-// eight 16-byte runs. The next tile is loaded into registers while the current
-// one is used, so global latency hides behind the MFMA work.
+// row-major [64 keys][D] with their 16-byte chunks XOR-swizzled by row (no bank
+// conflicts for either operand read). Wavefronts 0-3 stage K and 4-7 stage V,
+// one block each, through registers: the next-but-one tile is loaded while the
+// current one is used and stored at its end (one barrier per tile).
 // Per wavefront (32 rows) and tile, with MFMA 32x32x16 bf16:
 //   S^T[32 keys x 32 rows] = K . Q^T for each 32-key half (D/16 MFMAs each;
-//     Q^T stays in registers). Lane (col = lane%32, half = lane/32) holds keys
-//     8(i/4) + 4 half + i%4 (i = 0..15) of row col, so a row's softmax needs
-//     one cross-lane step.
+//     Q^T stays in registers; K operands are read four chunks ahead). Lane
+//     (col = lane%32, half = lane/32) holds keys 8(i/4) + 4 half + i%4
+//     (i = 0..15) of row col, so a row's softmax needs one cross-lane step.
 //   O^T[32 dims x 32 rows] += V^T . P^T (4 MFMAs of 16 keys per 32 dims):
-//     P^T is the lane's own probabilities (bf16); V^T comes from two transposed
-//     8-byte LDS reads whose key order matches P.
+//     P^T is the lane's own probabilities (bf16); V^T comes from two
+//     transposed 8-byte LDS reads (ds_read_b64_tr_b16) whose key order matches
+//     P, read four products ahead.
 // fp32 online softmax in log2 units (one FMA and one v_exp_f32 per score), fp32
 // accumulation; the running max moves only when a tile exceeds it by 2^8, so the
 // output is rescaled rarely (exact: numerator and denominator share the max).
@@ -50,14 +50,21 @@ typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 // Physical 16-byte chunk of logical chunk `ch` in row `row` of a staged tile.
 // K rows: the row's low 4 bits (16-lane K reads hit 16 distinct chunks).
-// V rows: 2 x (row & 3), so the 4 consecutive keys of a transposed read fall on
-// 8 distinct chunks.
+// V rows: a transposed read by 32 lanes covers 4 consecutive keys x 32 dims,
+// i.e. 4 logical chunks of 4 rows; the XOR spreads those 16 pieces over 16
+// distinct bank groups (D = 128: rows are 256 B, one full pass over the 64
+// banks, so the XOR takes 4 x (row & 3); D = 64: rows are 128 B and alternate
+// bank halves, so rows 2 apart are told apart by 4 x ((row >> 1) & 1)).
 template <int kCh>
 __device__ __forceinline__ int k_phys(int row, int ch) {
   if constexpr (kCh == 16) return ch ^ (row & 15);
   else return ch ^ ((row >> 1) & 7);
 }
-__device__ __forceinline__ int v_phys(int row, int ch) { return ch ^ (2 * (row & 3)); }
+template <int kCh>
+__device__ __forceinline__ int v_phys(int row, int ch) {
+  if constexpr (kCh == 16) return ch ^ (4 * (row & 3));
+  else return ch ^ (4 * ((row >> 1) & 1));
+}
 
 template <int D, int G>
 __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a) {
@@ -128,7 +135,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
   for (int i = 0; i < kInstr; ++i) {
     const int slot = (sblk * kInstr + i) * 64 + lane;
     const int row = slot / kCh;
-    const int ch = s_is_v ? v_phys(row, slot % kCh) : k_phys<kCh>(row, slot % kCh);
+    const int ch = s_is_v ? v_phys<kCh>(row, slot % kCh) : k_phys<kCh>(row, slot % kCh);
     src_off[i] = (row & 15) * row_elems + kvh * D + 8 * ch;
   }
   u32x4 sreg[kInstr];
@@ -176,7 +183,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) {
       const int dim = 32 * dt + 16 * (g & 1) + 4 * (i & 3);
-      v_addr[dt] = vs0 + 16u * (vrow * kCh + v_phys(vrow, dim >> 3)) + 2u * (dim & 7);
+      v_addr[dt] = vs0 + 16u * (vrow * kCh + v_phys<kCh>(vrow, dim >> 3)) + 2u * (dim & 7);
     }
   }
 
@@ -204,20 +211,28 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
       for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
     {
       typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
-      u32x4 ka[2][2];  // operands of chunk c (ping) and c+1 (pong)
+      // K operands run kAhead chunks ahead of the MFMAs that use them, so LDS
+      // latency hides behind the MFMAs of the chunks in between
+      constexpr int kAhead = 4;
+      u32x4 ka[kAhead][2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-        ka[0][kb] = *(lds_u32x4*)(uintptr_t)(k_addr[0] + koff + kb * 32 * kCh * 16);
-#pragma unroll
-      for (int c = 0; c < D / 16; ++c) {
-        if (c + 1 < D / 16) {
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-            ka[(c + 1) & 1][kb] = *(lds_u32x4*)(uintptr_t)(k_addr[c + 1] + koff + kb * 32 * kCh * 16);
-        }
+      for (int c = 0; c < kAhead; ++c)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
-          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[c & 1][kb]), as_bf16x8(qb[c]), sacc[kb], 0, 0, 0);
+          ka[c][kb] = *(lds_u32x4*)(uintptr_t)(k_addr[c] + koff + kb * 32 * kCh * 16);
+      __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the MFMAs
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[c % kAhead][kb]), as_bf16x8(qb[c]),
+                                                             sacc[kb], 0, 0, 0);
+        if (c + kAhead < D / 16) {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+            ka[c % kAhead][kb] = *(lds_u32x4*)(uintptr_t)(k_addr[c + kAhead] + koff + kb * 32 * kCh * 16);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     // scores are transformed in place: raw -> masked -> probability
@@ -265,16 +280,29 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
       pb[u] = u32x4{pack_bf16x2(e[b], e[b + 1]), pack_bf16x2(e[b + 2], e[b + 3]),
                     pack_bf16x2(e[b + 4], e[b + 5]), pack_bf16x2(e[b + 6], e[b + 7])};
     }
+    {
+      // V^T operands (two transposed reads each) run kAhead products ahead of
+      // their MFMAs. Product j is (u = j / (D/32), dt = j % (D/32)); its operand
+      // holds keys 16u + 4 half + 0..3 and 16u + 8 + 4 half + 0..3.
+      constexpr int kProducts = 4 * (D / 32);
+      constexpr int kAhead = 4;
+      v4i16 vlo[kAhead], vhi[kAhead];
+      auto vread = [&](int j, int r) {
+        const uint32_t base = v_addr[j % (D / 32)] + voff + (j / (D / 32)) * 16 * kCh * 16;
+        vlo[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(uintptr_t)base);
+        vhi[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(uintptr_t)(base + 8 * kCh * 16));
+      };
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+      for (int j = 0; j < kAhead; ++j) vread(j, j);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
-        // keys 16u + 4 half + 0..3 (rr = 0) and 16u + 8 + 4 half + 0..3 (rr = 1)
-        const uint32_t base = v_addr[dt] + voff + u * 16 * kCh * 16;
-        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(uintptr_t)base);
-        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(uintptr_t)(base + 8 * kCh * 16));
-        const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      for (int j = 0; j < kProducts; ++j) {
+        const bf16x8 va =
+            __builtin_bit_cast(bf16x8, __builtin_shufflevector(vlo[j % kAhead], vhi[j % kAhead], 0, 1, 2, 3, 4, 5, 6, 7));
+        const int dt = j % (D / 32), u = j / (D / 32);
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, as_bf16x8(pb[u]), o[dt], 0, 0, 0);
+        if (j + kAhead < kProducts) vread(j + kAhead, j % kAhead);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     // tile t+1 goes to the other stage, last read by tile t-1 (before the last barrier)
