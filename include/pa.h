@@ -169,6 +169,28 @@ int pa_prefill_chunk(const pa_cache_desc* desc, void* out, const void* q,
 int pa_copy_blocks(const pa_cache_desc* desc, void* k_cache, void* v_cache,
                    const int32_t* block_pairs, int64_t num_pairs, void* stream);
 
+/* Move whole blocks (K and V alike) between the device pool and a swap pool in
+ * host memory: the swap-out/in that lets a preempted request keep its computed
+ * K/V in CPU memory instead of recomputing it (aitrending, "The 1960s Operating
+ * System Trick That Makes vLLM 4x Faster", Technical Details: preemption by
+ * swapping to CPU memory or by recomputation).
+ *   host_k, host_v   [num_host_blocks][16][Hkv][D], same element type as the
+ *                    pool, in pinned host memory that the GPU can address
+ *                    (hipHostMalloc, or torch pin_memory=True); other memory
+ *                    is refused with PA_ERR_INVALID_ARG before any launch.
+ *   block_pairs      device int32 [num_pairs][2]:
+ *                    direction PA_SWAP_OUT: (device block, host block), device -> host;
+ *                    direction PA_SWAP_IN:  (host block, device block), host -> device.
+ * Destinations are distinct within a call (check mode verifies this); pairs
+ * outside either pool are skipped. The copy is bit-exact. Run a step's swap-out
+ * before its swap-in, copy-on-write copies and KV writes: blocks a swap-out
+ * frees may be handed out again in the same step. */
+#define PA_SWAP_OUT 0
+#define PA_SWAP_IN 1
+int pa_swap_blocks(const pa_cache_desc* desc, void* k_cache, void* v_cache, void* host_k,
+                   void* host_v, int64_t num_host_blocks, const int32_t* block_pairs,
+                   int64_t num_pairs, int32_t direction, void* stream);
+
 /* Copy each request's logical K and V out of the pool through its block table,
  * bit for bit, using the same addressing as the attention kernels (an
  * inspection aid for tests).

@@ -9,6 +9,7 @@ from .paged_attention import (  # noqa: F401
     slot_location,
     write_kv,
     copy_blocks,
+    swap_blocks,
     blocks_for,
     gather_logical,
     kv_head_of,

@@ -114,6 +114,31 @@ def copy_blocks(k_pool, v_pool, block_pairs) -> None:
         v_pool[b] = v_pool[a]
 
 
+def swap_blocks(k_pool, v_pool, host_k, host_v, block_pairs, to_host: bool) -> None:
+    """Move whole blocks between the device pool and a host swap pool, K and V alike.
+
+    Preemption may keep a request's K/V by swapping its blocks to CPU memory
+    instead of recomputing them (aitrending, "The 1960s Operating System Trick
+    That Makes vLLM 4x Faster", Technical Details). to_host: pairs are
+    (device block, host block); otherwise (host block, device block).
+    Destinations must be distinct.
+    """
+    pairs = np.asarray(block_pairs, dtype=np.int64).reshape(-1, 2)
+    dst = pairs[:, 1].tolist()
+    if len(set(dst)) != len(dst):
+        raise ValueError("a block is a destination twice")
+    for a, b in pairs.tolist():
+        dev, hst = (a, b) if to_host else (b, a)
+        if not (0 <= dev < k_pool.shape[0] and 0 <= hst < host_k.shape[0]):
+            raise IndexError("block pair outside a pool")
+        if to_host:
+            host_k[hst] = k_pool[dev]
+            host_v[hst] = v_pool[dev]
+        else:
+            k_pool[dev] = host_k[hst]
+            v_pool[dev] = host_v[hst]
+
+
 def blocks_for(num_tokens: int) -> int:
     """Blocks covering num_tokens tokens: ceil(num_tokens / 16)."""
     return (int(num_tokens) + BLOCK_SIZE - 1) // BLOCK_SIZE

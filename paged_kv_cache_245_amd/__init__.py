@@ -9,6 +9,8 @@ from ._lib import (  # noqa: F401
     EXPORTED,
     PA_BF16,
     PA_F32,
+    PA_SWAP_IN,
+    PA_SWAP_OUT,
     CacheDesc,
     PAError,
     cache_desc,
@@ -25,6 +27,7 @@ from ._lib import (  # noqa: F401
     pa_last_error_detail,
     pa_prefill_chunk,
     pa_strerror,
+    pa_swap_blocks,
     pa_version,
     pa_write_kv,
     torch_dtype,

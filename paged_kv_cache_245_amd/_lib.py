@@ -20,7 +20,7 @@ PA_BF16 = 1
 BLOCK_SIZE = 16
 
 EXPORTED = ("pa_write_kv", "pa_decode_partition_tokens", "pa_decode_workspace_size", "pa_decode",
-            "pa_prefill_chunk", "pa_copy_blocks", "pa_gather_kv", "pa_strerror", "pa_last_error_detail",
+            "pa_prefill_chunk", "pa_copy_blocks", "pa_swap_blocks", "pa_gather_kv", "pa_strerror", "pa_last_error_detail",
             "pa_version", "pa_bench_copy", "pa_bench_read", "pa_bench_flush")
 
 
@@ -69,6 +69,7 @@ def load():
         "pa_decode": (ctypes.c_int, [D, P, P, P, P, P, I32, P, I32, I32, F, I32, P, SZ, P]),
         "pa_prefill_chunk": (ctypes.c_int, [D, P, P, P, P, P, P, P, I32, I32, I32, I32, I32, F, P]),
         "pa_copy_blocks": (ctypes.c_int, [D, P, P, P, I64, P]),
+        "pa_swap_blocks": (ctypes.c_int, [D, P, P, P, P, I64, P, I64, I32, P]),
         "pa_gather_kv": (ctypes.c_int, [D, P, P, P, P, P, I32, P, I32, I32, P]),
         "pa_strerror": (ctypes.c_char_p, [ctypes.c_int]),
         "pa_last_error_detail": (ctypes.c_char_p, []),
@@ -202,6 +203,30 @@ def pa_copy_blocks(desc, k_cache, v_cache, block_pairs, stream=None):
     st = load().pa_copy_blocks(ctypes.byref(desc), _ptr(k_cache), _ptr(v_cache), _ptr(block_pairs),
                                block_pairs.shape[0], _stream(stream, k_cache))
     _check(st, "pa_copy_blocks")
+
+
+PA_SWAP_OUT = 0
+PA_SWAP_IN = 1
+
+
+def pa_swap_blocks(desc, k_cache, v_cache, host_k, host_v, block_pairs, direction, stream=None):
+    """host_k/host_v: pinned CPU tensors [NH, 16, Hkv, D]; block_pairs int32 [n, 2] on the GPU:
+    (device, host) for PA_SWAP_OUT, (host, device) for PA_SWAP_IN."""
+    dt = torch_dtype(desc)
+    for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache"), (host_k, "host_k"), (host_v, "host_v")):
+        _need(t, dt, n)
+    if host_k.is_cuda or host_v.is_cuda or not host_k.is_pinned() or not host_v.is_pinned():
+        raise ValueError("host_k/host_v must be pinned CPU tensors")
+    if host_k.shape != host_v.shape or not host_k.is_contiguous() or not host_v.is_contiguous():
+        raise ValueError("host_k/host_v must be contiguous and of one shape")
+    _need(block_pairs, torch.int32, "block_pairs", 2)
+    if block_pairs.shape[1] != 2:
+        raise ValueError("block_pairs must be [n, 2]")
+    st = load().pa_swap_blocks(ctypes.byref(desc), _ptr(k_cache), _ptr(v_cache),
+                               ctypes.c_void_p(host_k.data_ptr()), ctypes.c_void_p(host_v.data_ptr()),
+                               host_k.shape[0], _ptr(block_pairs), block_pairs.shape[0], int(direction),
+                               _stream(stream, k_cache))
+    _check(st, "pa_swap_blocks")
 
 
 def pa_gather_kv(desc, dst_k, dst_v, k_cache, v_cache, block_tables, context_lens,

@@ -387,6 +387,69 @@ int pa_copy_blocks(const pa_cache_desc* desc, void* k_cache, void* v_cache,
                     "copy_blocks launch");
 }
 
+namespace {
+// Device-visible address of pinned host memory holding `bytes` bytes at `p`, or
+// nullptr if `p` is not such memory (pageable memory would fault on the GPU).
+void* host_device_pointer(void* p, size_t bytes) {
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  if (attr.type != hipMemoryTypeHost || attr.devicePointer == nullptr) return nullptr;
+  void* base = nullptr;
+  size_t size = 0;
+  if (hipMemGetAddressRange(&base, &size, attr.devicePointer) == hipSuccess && base != nullptr) {
+    const size_t off = (size_t)((char*)attr.devicePointer - (char*)base);
+    if (off > size || size - off < bytes) return nullptr;  // the buffer is too small
+  } else {
+    (void)hipGetLastError();
+  }
+  return attr.devicePointer;
+}
+}  // namespace
+
+int pa_swap_blocks(const pa_cache_desc* desc, void* k_cache, void* v_cache, void* host_k,
+                   void* host_v, int64_t num_host_blocks, const int32_t* block_pairs,
+                   int64_t num_pairs, int32_t direction, void* stream) {
+  int st = validate_desc(desc);
+  if (st != PA_OK) return st;
+  if (num_pairs < 0) return fail(PA_ERR_INVALID_ARG, "num_pairs is negative");
+  if (direction != PA_SWAP_OUT && direction != PA_SWAP_IN)
+    return fail(PA_ERR_INVALID_ARG, "direction must be PA_SWAP_OUT or PA_SWAP_IN");
+  if (num_host_blocks < 1) return fail(PA_ERR_INVALID_ARG, "num_host_blocks must be >= 1");
+  if (num_pairs == 0) return PA_OK;
+  if (num_pairs > INT32_MAX) return fail(PA_ERR_UNSUPPORTED, "too many pairs");
+  if (!k_cache || !v_cache || !host_k || !host_v || !block_pairs)
+    return fail(PA_ERR_INVALID_ARG, "null pointer argument");
+  const int64_t block_bytes =
+      (int64_t)PA_BLOCK_SIZE * desc->num_kv_heads * desc->head_dim * elem_bytes(desc->dtype);
+  void* dk = host_device_pointer(host_k, (size_t)(num_host_blocks * block_bytes));
+  void* dv = host_device_pointer(host_v, (size_t)(num_host_blocks * block_bytes));
+  if (dk == nullptr || dv == nullptr)
+    return fail(PA_ERR_INVALID_ARG, "host_k/host_v must be pinned host memory of num_host_blocks blocks");
+  if (check_mode()) {
+    if (hipStreamSynchronize(as_stream(stream)) != hipSuccess)
+      return fail(PA_ERR_HIP, "stream synchronize failed");
+    std::vector<int32_t> pairs;
+    if (!fetch(pairs, block_pairs, (size_t)num_pairs * 2)) return fail(PA_ERR_HIP, "copy of pairs failed");
+    std::unordered_set<int32_t> dsts;
+    const bool out = direction == PA_SWAP_OUT;
+    for (int64_t i = 0; i < num_pairs; ++i) {
+      const int32_t dev = out ? pairs[2 * i] : pairs[2 * i + 1];
+      const int32_t hst = out ? pairs[2 * i + 1] : pairs[2 * i];
+      if (dev < 0 || dev >= desc->num_blocks || hst < 0 || hst >= num_host_blocks)
+        return fail(PA_ERR_RANGE, "pair " + std::to_string(i) + " is outside a pool");
+      if (!dsts.insert(pairs[2 * i + 1]).second)
+        return fail(PA_ERR_RANGE, "block " + std::to_string(pairs[2 * i + 1]) + " is a destination twice");
+    }
+  }
+  return hip_status(pa::launch_swap_blocks(k_cache, v_cache, dk, dv, block_pairs, num_pairs, block_bytes,
+                                           desc->num_blocks, num_host_blocks, direction == PA_SWAP_OUT,
+                                           as_stream(stream)),
+                    "swap_blocks launch");
+}
+
 int pa_gather_kv(const pa_cache_desc* desc, void* dst_k, void* dst_v, const void* k_cache,
                  const void* v_cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
                  const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,

@@ -132,6 +132,12 @@ hipError_t launch_gather_kv(void* dst_k, void* dst_v, const void* k_cache, const
                             int64_t num_blocks, hipStream_t stream);
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int64_t num_pairs,
                               int64_t block_bytes, int64_t num_blocks, hipStream_t stream);
+// Copies whole blocks between the device pool and a host swap pool (pointers the
+// device can address); to_host: pairs are (device, host), else (host, device).
+hipError_t launch_swap_blocks(void* k_cache, void* v_cache, void* host_k, void* host_v,
+                              const int32_t* pairs, int64_t num_pairs, int64_t block_bytes,
+                              int64_t num_blocks, int64_t num_host_blocks, bool to_host,
+                              hipStream_t stream);
 hipError_t launch_bench_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
 hipError_t launch_bench_read(const void* src, size_t bytes, float* sink, hipStream_t stream);
 hipError_t launch_bench_flush(void* buf, size_t bytes, hipStream_t stream);

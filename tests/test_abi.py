@@ -153,3 +153,25 @@ def test_binding_refuses_host_tensors(lib):
     x = torch.zeros(4, 8, 64)
     with pytest.raises(ValueError):
         pa.pa_write_kv(d, x, x, x, x, torch.zeros(4, dtype=torch.int32))
+
+
+def test_swap_and_copy_argument_checks(lib):
+    fake = ctypes.c_void_p(0x1000)
+    d = desc()
+    # direction, counts and null pointers are refused before anything touches the GPU
+    assert lib.pa_swap_blocks(ctypes.byref(d), fake, fake, fake, fake, 4, fake, 1, 7, None) == INVALID
+    assert lib.pa_swap_blocks(ctypes.byref(d), fake, fake, fake, fake, 0, fake, 1, 0, None) == INVALID
+    assert lib.pa_swap_blocks(ctypes.byref(d), fake, fake, fake, fake, 4, fake, -1, 0, None) == INVALID
+    assert lib.pa_swap_blocks(ctypes.byref(d), fake, fake, fake, fake, 4, fake, 0, 1, None) == PA_OK
+    assert lib.pa_swap_blocks(ctypes.byref(d), fake, fake, None, fake, 4, fake, 2, 1, None) == INVALID
+    assert lib.pa_copy_blocks(ctypes.byref(d), fake, fake, fake, -1, None) == INVALID
+    assert lib.pa_copy_blocks(ctypes.byref(d), fake, fake, fake, 0, None) == PA_OK
+    assert lib.pa_copy_blocks(ctypes.byref(d), fake, None, fake, 3, None) == INVALID
+
+
+def test_swap_binding_needs_pinned_host_tensors(lib):
+    import torch
+    d = desc(dtype="f32", num_q_heads=8, num_kv_heads=8, head_dim=64)
+    x = torch.zeros(2, 16, 8, 64)
+    with pytest.raises(ValueError):
+        pa.pa_swap_blocks(d, x, x, x, x, torch.zeros(1, 2, dtype=torch.int32), pa.PA_SWAP_OUT)

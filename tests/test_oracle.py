@@ -289,6 +289,42 @@ def pin_copy_on_write_fork():
     assert np.max(np.abs(got[0] - ref[0])) <= 1e-12
 
 
+def pin_swap_round_trip():
+    """Blocks swapped out land bit-exact in the host pool; swapped back into other device
+    blocks, a request reads the same logical context through its new table (the decode
+    result is identical), and no other block changes."""
+    w = custom_decode(47, [40, 9], Hq=4, Hkv=2, D=8, dtype="bf16", num_blocks=12)
+    k, v = oracle_pools(w)
+    d = w.decode
+    before = oracle.decode(d.q, k, v, d.block_tables, d.context_lens, "bf16")
+    table = d.block_tables[0, :3].tolist()
+    hk = oracle.empty_pool(5, 2, 8, "bf16", 0)
+    hv = hk.copy()
+    k0, v0 = k.copy(), v.copy()
+    pa_oracle.swap_blocks(k, v, hk, hv, [[b, h] for b, h in zip(table, (4, 0, 2))], True)
+    assert np.array_equal(k, k0) and np.array_equal(v, v0)
+    assert np.array_equal(hk[[4, 0, 2]], k0[table]) and np.array_equal(hv[[4, 0, 2]], v0[table])
+    assert not hk[[1, 3]].any() and not hv[[1, 3]].any()
+    used = set(d.block_tables.ravel().tolist())
+    fresh = [b for b in range(k.shape[0]) if b not in used][:3]
+    assert len(fresh) == 3
+    k[table] = 0x7FC0  # the old blocks are handed to someone else
+    v[table] = 0x7FC0
+    k1, v1 = k.copy(), v.copy()
+    pa_oracle.swap_blocks(k, v, hk, hv, [[h, b] for h, b in zip((4, 0, 2), fresh)], False)
+    assert np.array_equal(k[fresh], k0[table]) and np.array_equal(v[fresh], v0[table])
+    others = [b for b in range(k.shape[0]) if b not in fresh]
+    assert np.array_equal(k[others], k1[others]) and np.array_equal(v[others], v1[others])
+    tables = d.block_tables.copy()
+    tables[0, :3] = fresh
+    after = oracle.decode(d.q, k, v, tables, d.context_lens, "bf16", pairs=[(0, h) for h in range(4)])
+    assert np.array_equal(after[0], before[0])
+    with pytest.raises((ValueError, IndexError)):
+        pa_oracle.swap_blocks(k, v, hk, hv, [[0, 1], [2, 1]], True)
+    with pytest.raises((ValueError, IndexError)):
+        pa_oracle.swap_blocks(k, v, hk, hv, [[0, 5]], True)
+
+
 def pin_empty_context_rejected():
     k = oracle.empty_pool(2, 1, 4, "f32", 0)
     with pytest.raises(ValueError):
@@ -302,6 +338,7 @@ ALL_PINS = [
     pin_softmax_weights, pin_permutation_invariance, pin_prefix_sharing,
     pin_gqa_equals_repeated_mha, pin_chunk_is_rows_of_full, pin_decode_is_one_row_chunk,
     pin_split_kv_identity, pin_empty_context_rejected, pin_copy_blocks, pin_copy_on_write_fork,
+    pin_swap_round_trip,
 ]
 
 
@@ -359,6 +396,11 @@ MISTAKES = {
         "copy_blocks",
         lambda kp, vp, pairs: [kp.__setitem__(int(a), kp[int(b)]) or vp.__setitem__(int(a), vp[int(b)])
                                for a, b in np.asarray(pairs).reshape(-1, 2)] and None),
+    "swap ignores its direction": (
+        "swap_blocks",
+        lambda kp, vp, hk, hv, pairs, to_host: [
+            (hk.__setitem__(int(b), kp[int(a)]), hv.__setitem__(int(b), vp[int(a)]))
+            for a, b in np.asarray(pairs).reshape(-1, 2)] and None),
     "table read backwards": (
         "gather_logical",
         lambda pool, row, L: pool[np.asarray(row[:(L + 15) // 16])[::-1]].reshape(
