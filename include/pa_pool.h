@@ -21,8 +21,12 @@
  *   - Forked requests (parallel sampling) share all blocks; the first write
  *     into a shared, partly filled block makes a private copy (copy-on-write:
  *     aitrending, "The 1960s Operating System Trick That Makes vLLM 4x Faster",
- *     Technical Details). The copies are queued for the caller, who runs them
- *     with pa_copy_blocks before the step's pa_write_kv.
+ *     Technical Details).
+ *   - A preempted request may keep its computed K/V by swapping its blocks out
+ *     to a swap space in CPU memory, and swap them in when it resumes (same
+ *     page and section; the alternative is recomputation).
+ *   - Copies and swaps are queued for the caller as one ordered list of block
+ *     operations, run on the device before the step's KV writes.
  *
  * Readings where the pages are silent:
  *   - Blocks needed for a request = ceil(tokens it will hold / 16) minus the
@@ -61,6 +65,10 @@ typedef struct pa_block_pool pa_block_pool;
 /* A pool of num_blocks (>= 1) blocks. prefix_caching: 0 off, 1 on.
  * Returns NULL on a bad argument or when host memory runs out. */
 pa_block_pool* pa_pool_create(int64_t num_blocks, int32_t prefix_caching);
+/* The same with a swap space of num_host_blocks (>= 0) blocks in CPU memory, for
+ * pa_pool_swap_out / pa_pool_swap_in (pa_pool_create has none). */
+pa_block_pool* pa_pool_create_with_swap(int64_t num_blocks, int64_t num_host_blocks,
+                                        int32_t prefix_caching);
 void pa_pool_destroy(pa_block_pool* pool);
 
 /* Register request req_id (unused id, >= 0) with its prompt tokens [num_tokens >= 1].
@@ -81,7 +89,7 @@ int64_t pa_pool_prefix_hit_tokens(const pa_block_pool* pool, int64_t req_id);
  * pa_pool_prefix_hit_tokens reports), which advances its computed count; the
  * hit token count goes to *hit_tokens (may be NULL). If the block that the new
  * tokens start in is partly filled and shared, the request gets a private copy
- * of it (queued, see pa_pool_take_copies). Returns 0, PA_POOL_NO_SPACE (nothing changed), or
+ * of it (queued as a PA_POOL_OP_COPY operation, see pa_pool_take_ops). Returns 0, PA_POOL_NO_SPACE (nothing changed), or
  * an error (computed + hits + num_new_tokens beyond the request's tokens). */
 int pa_pool_allocate_slots(pa_block_pool* pool, int64_t req_id, int64_t num_new_tokens,
                            int64_t* hit_tokens);
@@ -100,10 +108,40 @@ int pa_pool_free_request(pa_block_pool* pool, int64_t req_id, int32_t keep_reque
  * sharing the blocks that hold the computed tokens (one more reference each). */
 int pa_pool_fork(pa_block_pool* pool, int64_t parent_id, int64_t child_id);
 
-/* Move up to max_pairs pending copy-on-write pairs (source block, destination
- * block) into pairs[2*i], pairs[2*i+1], oldest first; returns how many were
- * moved (the rest stay queued). */
-int64_t pa_pool_take_copies(pa_block_pool* pool, int32_t* pairs, int64_t max_pairs);
+/* Swap-out (preemption that keeps the K/V instead of recomputing it:
+ * aitrending, "The 1960s Operating System Trick That Makes vLLM 4x Faster",
+ * Technical Details). The blocks holding the request's computed tokens are
+ * paired with free host blocks, in order, and queued as (device, host) pairs;
+ * then all its device blocks are released as by pa_pool_free_request. The
+ * request keeps its tokens and computed count and is "swapped": it holds no
+ * device blocks and cannot be allocated, committed or forked until swapped in.
+ * PA_POOL_NO_SPACE (nothing changed) if the swap space is short. A request with
+ * nothing computed just releases its blocks and is not swapped. The pairs are
+ * queued as PA_POOL_OP_SWAP_OUT operations (see pa_pool_take_ops). */
+int pa_pool_swap_out(pa_block_pool* pool, int64_t req_id);
+/* Swap-in: one device block per host block, from the head of the free queue as
+ * an allocation would take them, queued as PA_POOL_OP_SWAP_IN operations; the
+ * request is running again with its computed count, and its host blocks are
+ * free again. PA_POOL_NO_SPACE (nothing changed) if the free queue is short. */
+int pa_pool_swap_in(pa_block_pool* pool, int64_t req_id);
+/* 1 if the request is swapped out, 0 if not, negative if unknown. */
+int32_t pa_pool_request_swapped(const pa_block_pool* pool, int64_t req_id);
+int64_t pa_pool_num_free_host_blocks(const pa_block_pool* pool);
+/* Block operations for the device, in the order the pool performed them:
+ * copy-on-write copies (allocate_slots), swap-outs and swap-ins. Moves up to
+ * max_ops of them into ops[3 i .. 3 i + 2] = (kind, source, destination),
+ * oldest first; returns how many were moved (the rest stay queued).
+ *   PA_POOL_OP_COPY      device block -> device block (pa_copy_blocks)
+ *   PA_POOL_OP_SWAP_OUT  device block -> host block   (pa_swap_blocks, PA_SWAP_OUT)
+ *   PA_POOL_OP_SWAP_IN   host block   -> device block (pa_swap_blocks, PA_SWAP_IN)
+ * Run them in this order, all before the KV writes of the step that follows:
+ * a block freed by one operation may be handed out again by a later one.
+ * Consecutive operations of one kind may run as one call when none of them
+ * writes a block that another of them reads or writes. */
+#define PA_POOL_OP_COPY 0
+#define PA_POOL_OP_SWAP_OUT 1
+#define PA_POOL_OP_SWAP_IN 2
+int64_t pa_pool_take_ops(pa_block_pool* pool, int32_t* ops, int64_t max_ops);
 
 /* Queries. Request queries return a negative status for an unknown request. */
 int64_t pa_pool_num_blocks(const pa_block_pool* pool);

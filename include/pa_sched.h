@@ -15,7 +15,11 @@
  *     priority, then latest arrival, under priority scheduling). The victim's
  *     blocks are released, its computed count goes back to 0 and it returns to
  *     the head of the waiting queue, to be recomputed; its cached prefix blocks
- *     may still be found in the pool when it is admitted again.
+ *     may still be found in the pool when it is admitted again. With
+ *     PA_SCHED_SWAP the victim's computed K/V is swapped out to the pool's host
+ *     swap space instead, when it has room, and swapped back in when the request
+ *     is admitted again (aitrending, "The 1960s Operating System Trick That
+ *     Makes vLLM 4x Faster", Technical Details: swap or recompute).
  *
  * Readings where the pages are silent:
  *   - No waiting request is admitted in a step that preempted.
@@ -24,6 +28,9 @@
  *   - Under priority scheduling the waiting queue is ordered by (priority,
  *     arrival), lower value first; a victim already scheduled in the same step
  *     is taken out of the step again.
+ *   - A swapped request is admitted only if the free queue covers both its
+ *     swap-in and the blocks of the tokens it is given; it resumes at its
+ *     computed count. A swap space too small for the victim means recompute.
  *   - When a request's computed count reaches its token count, the step's
  *     sampled token for it is appended; it finishes when it has produced
  *     max_new_tokens tokens (the last one is not appended).
@@ -32,8 +39,9 @@
  * requests given more than one token) and one pa_decode (those given one):
  * scheduled requests in batch order are the multi-token ones, then the
  * one-token ones, each group in scheduling order; new tokens are packed in the
- * same order. Copy-on-write pairs (forked requests) are taken from the pool
- * with pa_pool_take_copies and must run before the step's pa_write_kv.
+ * same order. The block operations the step caused (swap-outs, swap-ins,
+ * copy-on-write copies) are taken from the pool with pa_pool_take_ops and run,
+ * in order, before the step's pa_write_kv.
  *
  * Status codes are those of pa_pool.h. Not thread-safe; synchronous.
  */
@@ -50,12 +58,15 @@ extern "C" {
 
 #define PA_SCHED_FCFS 0
 #define PA_SCHED_PRIORITY 1
+#define PA_SCHED_RECOMPUTE 0
+#define PA_SCHED_SWAP 1
 
 typedef struct {
   int32_t max_num_batched_tokens; /* token budget of one step, >= 1 */
   int32_t max_num_seqs;           /* running requests at most, >= 1 */
   int32_t policy;                 /* PA_SCHED_FCFS or PA_SCHED_PRIORITY */
   int32_t chunked_prefill;        /* 1: a prompt may be split over steps */
+  int32_t preempt_mode;           /* PA_SCHED_RECOMPUTE or PA_SCHED_SWAP */
 } pa_sched_config;
 
 typedef struct pa_scheduler pa_scheduler;
@@ -103,6 +114,7 @@ int64_t pa_sched_update(pa_scheduler* sched, const int32_t* sampled);
 int64_t pa_sched_num_waiting(const pa_scheduler* sched);
 int64_t pa_sched_num_running(const pa_scheduler* sched);
 int64_t pa_sched_num_preemptions(const pa_scheduler* sched); /* since creation */
+int64_t pa_sched_num_swaps(const pa_scheduler* sched);       /* preemptions that swapped */
 /* Ids of finished requests, oldest first (up to max; removed once taken). */
 int64_t pa_sched_take_finished(pa_scheduler* sched, int64_t* ids, int64_t max);
 const char* pa_sched_last_error(void);

@@ -24,6 +24,8 @@ memory", unless noted):
   * Forked requests share blocks until one writes into a shared block; that
     block is copied first (aitrending, "The 1960s Operating System Trick That
     Makes vLLM 4x Faster", Technical Details, copy-on-write).
+  * A preempted request may keep its K/V by swapping its blocks to CPU memory
+    and swapping them back when it resumes (same page and section).
 
 Readings where the pages are silent (the same as the library's):
   * Blocks needed = ceil(tokens the request will hold / 16) - blocks it holds.
@@ -34,10 +36,15 @@ Readings where the pages are silent (the same as the library's):
   * A block whose prefix is already cached in another block stays uncached.
   * A fork shares the blocks that hold the parent's computed tokens; a write
     that starts inside a partly filled shared block first copies that block.
+  * A swap-out moves the blocks holding computed tokens, in order, to the first
+    free host blocks, then releases every device block as a free does; a swap-in
+    takes one device block per host block from the head of the free queue and
+    frees the host blocks. Copies and swaps form one ordered list of operations.
 """
 from __future__ import annotations
 
 BLOCK = 16
+OP_COPY, OP_SWAP_OUT, OP_SWAP_IN = 0, 1, 2  # kinds of block operations
 
 
 def ceil_blocks(tokens: int) -> int:
@@ -51,12 +58,14 @@ class Request:
         self.computed = 0
         self.hashed = 0      # full blocks already offered to the cache
         self.blocks = []
+        self.swapped = False
+        self.host_blocks = []
 
 
 class BlockPoolModel:
     """The pool as plain lists and dicts: `free` is the free queue, head at index 0."""
 
-    def __init__(self, num_blocks: int, prefix_caching: bool):
+    def __init__(self, num_blocks: int, prefix_caching: bool, num_host_blocks: int = 0):
         if num_blocks < 1:
             raise ValueError("num_blocks must be >= 1")
         self.prefix = bool(prefix_caching)
@@ -65,7 +74,8 @@ class BlockPoolModel:
         self.key_of = [None] * num_blocks   # prefix key a block caches, or None
         self.cache = {}                     # prefix key -> block
         self.reqs = {}
-        self.copies = []
+        self.ops = []                       # (kind, source, destination), in order
+        self.host_free = list(range(num_host_blocks))
 
     # ---------------------------------------------------------------- rules
     def prefix_key(self, r: Request, i: int):
@@ -110,7 +120,7 @@ class BlockPoolModel:
         self.reqs[rid].tokens.extend(tokens)
 
     def prefix_hits(self, r: Request):
-        if not self.prefix or r.blocks:
+        if not self.prefix or r.blocks or r.swapped:
             return []
         hits = []
         for i in range(self.max_hit_blocks(r)):
@@ -126,6 +136,8 @@ class BlockPoolModel:
     def allocate_slots(self, rid, n_new):
         """Returns the hit token count, or None when the free queue is too short."""
         r = self.reqs[rid]
+        if r.swapped:
+            raise ValueError("request is swapped out")
         hits = self.prefix_hits(r)
         start = r.computed + BLOCK * len(hits)
         total = start + n_new
@@ -150,7 +162,7 @@ class BlockPoolModel:
             dst = self.take_head()
             self.ref[src] -= 1
             r.blocks[first] = dst
-            self.copies.append((src, dst))
+            self.ops.append((OP_COPY, src, dst))
         for _ in range(fresh):
             r.blocks.append(self.take_head())
         return BLOCK * len(hits)
@@ -176,15 +188,53 @@ class BlockPoolModel:
             self.ref[b] -= 1
             if self.ref[b] == 0:
                 self.requeue(b)
+        self.host_free.extend(r.host_blocks)
         if keep:
             r.blocks, r.computed, r.hashed = [], 0, 0
+            r.host_blocks, r.swapped = [], False
         else:
             del self.reqs[rid]
+
+    def swap_out(self, rid):
+        """True, or False when the swap space is short (nothing changed)."""
+        r = self.reqs[rid]
+        if r.swapped:
+            raise ValueError("already swapped out")
+        keep = ceil_blocks(r.computed)
+        if keep > len(self.host_free):
+            return False
+        for i in range(keep):
+            h = self.host_free.pop(0)
+            self.ops.append((OP_SWAP_OUT, r.blocks[i], h))
+            r.host_blocks.append(h)
+        for b in self.release_order(r.blocks):
+            self.ref[b] -= 1
+            if self.ref[b] == 0:
+                self.requeue(b)
+        r.blocks, r.hashed, r.swapped = [], 0, keep > 0
+        return True
+
+    def swap_in(self, rid):
+        """True, or False when the free queue is short (nothing changed)."""
+        r = self.reqs[rid]
+        if not r.swapped:
+            raise ValueError("not swapped out")
+        if len(r.host_blocks) > len(self.free):
+            return False
+        for h in r.host_blocks:
+            d = self.take_head()
+            self.ops.append((OP_SWAP_IN, h, d))
+            r.blocks.append(d)
+            self.host_free.append(h)
+        r.host_blocks, r.swapped, r.hashed = [], False, 0
+        return True
 
     def fork(self, parent, child):
         if child in self.reqs or child < 0:
             raise ValueError("bad child id")
         p = self.reqs[parent]
+        if p.swapped:
+            raise ValueError("parent is swapped out")
         c = Request(p.tokens, p.salt)
         c.computed = p.computed
         c.hashed = min(p.hashed, p.computed // BLOCK)
@@ -193,8 +243,8 @@ class BlockPoolModel:
             self.ref[b] += 1
         self.reqs[child] = c
 
-    def take_copies(self):
-        out, self.copies = self.copies, []
+    def take_ops(self):
+        out, self.ops = self.ops, []
         return out
 
     def block_table(self, rid):

@@ -7,8 +7,10 @@
 // for shared prefixes, cached free blocks kept at the tail of the free queue
 // (evicted last) and a request's blocks released last block first. Forked
 // requests share blocks until one writes into a shared, partly filled block,
-// which is then copied (aitrending, "The 1960s Operating System Trick That
-// Makes vLLM 4x Faster", Technical Details).
+// which is then copied; a preempted request may keep its K/V by swapping its
+// blocks to a host swap space (aitrending, "The 1960s Operating System Trick
+// That Makes vLLM 4x Faster", Technical Details). Copies and swaps are queued
+// as one ordered list of block operations for the device.
 //
 // The free queue is an intrusive doubly linked list over block ids, so taking a
 // cached free block out of the middle on a prefix hit is O(1). The prefix cache
@@ -74,6 +76,8 @@ struct Request {
   int64_t computed = 0;
   int64_t hashed = 0;               // full blocks already offered to the cache
   std::vector<int32_t> blocks;
+  bool swapped = false;             // computed K/V lives in host_blocks
+  std::vector<int32_t> host_blocks;
   mutable std::vector<uint64_t> hashes;  // chained hashes of full blocks, grown on demand
 
   int64_t full_blocks() const { return (int64_t)tokens.size() / kB; }
@@ -96,7 +100,13 @@ struct pa_block_pool {
   bool prefix = false;
   std::unordered_map<uint64_t, int32_t> cache;
   std::unordered_map<int64_t, Request> reqs;
-  std::deque<std::pair<int32_t, int32_t>> copies;
+  // block operations for the device, in the order the pool performed them
+  struct Op {
+    int32_t kind, src, dst;
+  };
+  std::deque<Op> ops;
+  int64_t num_host = 0;
+  std::deque<int32_t> host_free;  // swap space, head first
 
   void unlink(int32_t id) {
     Block& b = blocks[id];
@@ -160,7 +170,7 @@ struct pa_block_pool {
   // Blocks a prefix hit would give request r now (leaving its last token to compute).
   std::vector<int32_t> prefix_hits(const Request& r) const {
     std::vector<int32_t> hits;
-    if (!prefix || !r.blocks.empty()) return hits;
+    if (!prefix || !r.blocks.empty() || r.swapped) return hits;
     const int64_t max_blocks = ((int64_t)r.tokens.size() - 1) / kB;
     for (int64_t i = 0; i < max_blocks; ++i) {
       const int32_t id = lookup(r, i);
@@ -186,8 +196,14 @@ int unknown(int64_t id) { return fail(PA_POOL_ERR_INVALID_ARG, "unknown request 
 extern "C" {
 
 pa_block_pool* pa_pool_create(int64_t num_blocks, int32_t prefix_caching) {
-  if (num_blocks < 1 || num_blocks > INT32_MAX / kB) {
-    fail(PA_POOL_ERR_INVALID_ARG, "num_blocks must be in [1, 2^31 / 16)");
+  return pa_pool_create_with_swap(num_blocks, 0, prefix_caching);
+}
+
+pa_block_pool* pa_pool_create_with_swap(int64_t num_blocks, int64_t num_host_blocks,
+                                        int32_t prefix_caching) {
+  if (num_blocks < 1 || num_blocks > INT32_MAX / kB || num_host_blocks < 0 ||
+      num_host_blocks > INT32_MAX / kB) {
+    fail(PA_POOL_ERR_INVALID_ARG, "num_blocks must be in [1, 2^31 / 16), num_host_blocks in [0, 2^31 / 16)");
     return nullptr;
   }
   pa_block_pool* p = new (std::nothrow) pa_block_pool;
@@ -201,6 +217,8 @@ pa_block_pool* pa_pool_create(int64_t num_blocks, int32_t prefix_caching) {
   }
   p->prefix = prefix_caching != 0;
   for (int32_t i = 0; i < (int32_t)num_blocks; ++i) p->push_tail(i);
+  p->num_host = num_host_blocks;
+  for (int32_t i = 0; i < (int32_t)num_host_blocks; ++i) p->host_free.push_back(i);
   return p;
 }
 
@@ -241,6 +259,7 @@ int pa_pool_allocate_slots(pa_block_pool* pool, int64_t req_id, int64_t num_new_
   Request* rp = pool->find(req_id);
   if (rp == nullptr) return unknown(req_id);
   Request& r = *rp;
+  if (r.swapped) return fail(PA_POOL_ERR_INVALID_ARG, "request is swapped out: swap it in first");
   const std::vector<int32_t> hits = pool->prefix_hits(r);
   const int64_t start = r.computed + (int64_t)hits.size() * kB;  // first token written
   const int64_t total = start + num_new_tokens;
@@ -270,7 +289,7 @@ int pa_pool_allocate_slots(pa_block_pool* pool, int64_t req_id, int64_t num_new_
     const int32_t dst = pool->pop_head();
     --pool->blocks[src].ref;  // was > 1
     r.blocks[first] = dst;
-    pool->copies.emplace_back(src, dst);
+    pool->ops.push_back({PA_POOL_OP_COPY, src, dst});
   }
   for (int64_t i = 0; i < fresh; ++i) r.blocks.push_back(pool->pop_head());
   if (hit_tokens != nullptr) *hit_tokens = (int64_t)hits.size() * kB;
@@ -311,8 +330,11 @@ int pa_pool_free_request(pa_block_pool* pool, int64_t req_id, int32_t keep_reque
   Request* rp = pool->find(req_id);
   if (rp == nullptr) return unknown(req_id);
   for (auto it = rp->blocks.rbegin(); it != rp->blocks.rend(); ++it) pool->release(*it);
+  for (int32_t h : rp->host_blocks) pool->host_free.push_back(h);
   if (keep_request) {
     rp->blocks.clear();
+    rp->host_blocks.clear();
+    rp->swapped = false;
     rp->computed = 0;
     rp->hashed = 0;
   } else {
@@ -327,6 +349,7 @@ int pa_pool_fork(pa_block_pool* pool, int64_t parent_id, int64_t child_id) {
   if (pool->reqs.count(child_id)) return fail(PA_POOL_ERR_INVALID_ARG, "request id in use");
   const Request* pp = pool->find(parent_id);
   if (pp == nullptr) return unknown(parent_id);
+  if (pp->swapped) return fail(PA_POOL_ERR_INVALID_ARG, "parent is swapped out");
   Request child;
   child.tokens = pp->tokens;
   child.salt = pp->salt;
@@ -340,13 +363,65 @@ int pa_pool_fork(pa_block_pool* pool, int64_t parent_id, int64_t child_id) {
   return PA_POOL_OK;
 }
 
-int64_t pa_pool_take_copies(pa_block_pool* pool, int32_t* pairs, int64_t max_pairs) {
-  if (pool == nullptr || (max_pairs > 0 && pairs == nullptr)) return fail(PA_POOL_ERR_INVALID_ARG, "null pointer");
+int pa_pool_swap_out(pa_block_pool* pool, int64_t req_id) {
+  if (pool == nullptr) return fail(PA_POOL_ERR_INVALID_ARG, "null pointer");
+  Request* rp = pool->find(req_id);
+  if (rp == nullptr) return unknown(req_id);
+  Request& r = *rp;
+  if (r.swapped) return fail(PA_POOL_ERR_INVALID_ARG, "request is already swapped out");
+  const int64_t keep = (r.computed + kB - 1) / kB;  // blocks holding computed tokens
+  if (keep > (int64_t)pool->host_free.size()) return PA_POOL_NO_SPACE;
+  for (int64_t i = 0; i < keep; ++i) {
+    const int32_t h = pool->host_free.front();
+    pool->host_free.pop_front();
+    pool->ops.push_back({PA_POOL_OP_SWAP_OUT, r.blocks[i], h});
+    r.host_blocks.push_back(h);
+  }
+  for (auto it = r.blocks.rbegin(); it != r.blocks.rend(); ++it) pool->release(*it);
+  r.blocks.clear();
+  r.hashed = 0;
+  r.swapped = keep > 0;
+  return PA_POOL_OK;
+}
+
+int pa_pool_swap_in(pa_block_pool* pool, int64_t req_id) {
+  if (pool == nullptr) return fail(PA_POOL_ERR_INVALID_ARG, "null pointer");
+  Request* rp = pool->find(req_id);
+  if (rp == nullptr) return unknown(req_id);
+  Request& r = *rp;
+  if (!r.swapped) return fail(PA_POOL_ERR_INVALID_ARG, "request is not swapped out");
+  if ((int64_t)r.host_blocks.size() > pool->nfree) return PA_POOL_NO_SPACE;
+  for (int32_t h : r.host_blocks) {
+    const int32_t d = pool->pop_head();
+    pool->ops.push_back({PA_POOL_OP_SWAP_IN, h, d});
+    r.blocks.push_back(d);
+    pool->host_free.push_back(h);  // its copy-out precedes any later reuse in the op order
+  }
+  r.host_blocks.clear();
+  r.swapped = false;
+  r.hashed = 0;  // the next commit offers these full blocks to the prefix cache again
+  return PA_POOL_OK;
+}
+
+int32_t pa_pool_request_swapped(const pa_block_pool* pool, int64_t req_id) {
+  if (pool == nullptr) return fail(PA_POOL_ERR_INVALID_ARG, "null pointer");
+  const Request* r = pool->find(req_id);
+  return r ? (int32_t)r->swapped : unknown(req_id);
+}
+
+int64_t pa_pool_num_free_host_blocks(const pa_block_pool* pool) {
+  return pool ? (int64_t)pool->host_free.size() : fail(PA_POOL_ERR_INVALID_ARG, "null pointer");
+}
+
+int64_t pa_pool_take_ops(pa_block_pool* pool, int32_t* ops, int64_t max_ops) {
+  if (pool == nullptr || (max_ops > 0 && ops == nullptr)) return fail(PA_POOL_ERR_INVALID_ARG, "null pointer");
   int64_t n = 0;
-  while (n < max_pairs && !pool->copies.empty()) {
-    pairs[2 * n] = pool->copies.front().first;
-    pairs[2 * n + 1] = pool->copies.front().second;
-    pool->copies.pop_front();
+  while (n < max_ops && !pool->ops.empty()) {
+    const pa_block_pool::Op& o = pool->ops.front();
+    ops[3 * n] = o.kind;
+    ops[3 * n + 1] = o.src;
+    ops[3 * n + 2] = o.dst;
+    pool->ops.pop_front();
     ++n;
   }
   return n;

@@ -5,8 +5,9 @@
 // running requests first, in start order, each given what it lacks up to the
 // budget left; a request the pool cannot grow triggers preemption of the newest
 // running request (FCFS) or of the lowest-priority, latest-arrival one
-// (priority), which returns to the waiting queue with nothing computed; then,
-// unless the step preempted, waiting requests are admitted in queue order.
+// (priority), which returns to the waiting queue with nothing computed, or,
+// in swap mode, with its computed K/V swapped out to host memory; then, unless
+// the step preempted, waiting requests are admitted in queue order.
 #include "pa_sched.h"
 
 #include <algorithm>
@@ -48,6 +49,7 @@ struct pa_scheduler {
   std::vector<Item> plan;        // batch order
   std::deque<int64_t> finished;
   int64_t preemptions = 0;
+  int64_t swaps = 0;
   int64_t arrivals = 0;
 
   bool before(int64_t a, int64_t b) const {  // waiting order under priority scheduling
@@ -82,7 +84,8 @@ extern "C" {
 pa_scheduler* pa_sched_create(pa_block_pool* pool, const pa_sched_config* config) {
   if (pool == nullptr || config == nullptr || config->max_num_batched_tokens < 1 ||
       config->max_num_seqs < 1 ||
-      (config->policy != PA_SCHED_FCFS && config->policy != PA_SCHED_PRIORITY)) {
+      (config->policy != PA_SCHED_FCFS && config->policy != PA_SCHED_PRIORITY) ||
+      (config->preempt_mode != PA_SCHED_RECOMPUTE && config->preempt_mode != PA_SCHED_SWAP)) {
     fail(PA_POOL_ERR_INVALID_ARG, "bad pool or configuration");
     return nullptr;
   }
@@ -140,7 +143,14 @@ int64_t pa_sched_schedule(pa_scheduler* s) {
         budget += it->count;
         order.erase(it);
       }
-      pa_pool_free_request(s->pool, victim, 1);
+      bool swapped = false;
+      if (s->cfg.preempt_mode == PA_SCHED_SWAP) {
+        const int sst = pa_pool_swap_out(s->pool, victim);
+        if (sst < 0) return fail(sst, pa_pool_last_error());
+        swapped = sst == PA_POOL_OK && pa_pool_request_swapped(s->pool, victim) == 1;
+      }
+      if (swapped) ++s->swaps;
+      else pa_pool_free_request(s->pool, victim, 1);  // recompute later
       s->enqueue_waiting(victim, true);
       ++s->preemptions;
       preempted = true;
@@ -160,6 +170,24 @@ int64_t pa_sched_schedule(pa_scheduler* s) {
   while (!preempted && !s->waiting.empty() && budget > 0 &&
          (int64_t)s->running.size() < s->cfg.max_num_seqs) {
     const int64_t id = s->waiting.front();
+    if (pa_pool_request_swapped(s->pool, id) == 1) {
+      // resume at the computed count: swap in, then the blocks of the new tokens
+      const int64_t computed = pa_pool_request_computed(s->pool, id);
+      const int64_t lacking = pa_pool_request_tokens(s->pool, id) - computed;
+      if (!s->cfg.chunked_prefill && lacking > budget) break;
+      const int64_t n = std::min(lacking, budget);
+      const int64_t held = (computed + 15) / 16;
+      const int64_t need = std::max<int64_t>((computed + n + 15) / 16, held);
+      if (need > pa_pool_num_free_blocks(s->pool)) break;
+      int st = pa_pool_swap_in(s->pool, id);
+      if (st == PA_POOL_OK) st = pa_pool_allocate_slots(s->pool, id, n, nullptr);
+      if (st != PA_POOL_OK) return fail(st < 0 ? st : PA_POOL_ERR_INVALID_ARG, "swap-in admission failed");
+      s->waiting.pop_front();
+      s->running.push_back(id);
+      order.push_back(Item{id, (int32_t)computed, (int32_t)n});
+      budget -= n;
+      continue;
+    }
     const int64_t hit = pa_pool_prefix_hit_tokens(s->pool, id);
     const int64_t lacking = pa_pool_request_tokens(s->pool, id) - hit;
     if (!s->cfg.chunked_prefill && lacking > budget) break;
@@ -275,6 +303,9 @@ int64_t pa_sched_num_running(const pa_scheduler* s) {
 }
 int64_t pa_sched_num_preemptions(const pa_scheduler* s) {
   return s ? s->preemptions : fail(PA_POOL_ERR_INVALID_ARG, "null scheduler");
+}
+int64_t pa_sched_num_swaps(const pa_scheduler* s) {
+  return s ? s->swaps : fail(PA_POOL_ERR_INVALID_ARG, "null scheduler");
 }
 int64_t pa_sched_take_finished(pa_scheduler* s, int64_t* ids, int64_t max) {
   if (s == nullptr || (max > 0 && ids == nullptr)) return fail(PA_POOL_ERR_INVALID_ARG, "null pointer");

@@ -18,14 +18,16 @@ _host = None
 POOL_OK = 0
 POOL_NO_SPACE = 1
 BLOCK_SIZE = 16
+OP_COPY, OP_SWAP_OUT, OP_SWAP_IN = 0, 1, 2  # kinds of block operations (pa_pool_take_ops)
 
 POOL_EXPORTED = ("pa_pool_create", "pa_pool_destroy", "pa_pool_add_request", "pa_pool_append_tokens",
                  "pa_pool_prefix_hit_tokens", "pa_pool_allocate_slots", "pa_pool_commit",
-                 "pa_pool_free_request", "pa_pool_fork", "pa_pool_take_copies", "pa_pool_num_blocks",
+                 "pa_pool_free_request", "pa_pool_fork", "pa_pool_take_ops", "pa_pool_num_blocks",
                  "pa_pool_num_free_blocks", "pa_pool_num_cached_blocks", "pa_pool_ref_count",
                  "pa_pool_request_tokens", "pa_pool_request_computed", "pa_pool_block_table",
                  "pa_pool_slot_mapping", "pa_pool_free_queue", "pa_pool_block_hash",
-                 "pa_pool_last_error")
+                 "pa_pool_last_error", "pa_pool_create_with_swap", "pa_pool_swap_out",
+                 "pa_pool_swap_in", "pa_pool_request_swapped", "pa_pool_num_free_host_blocks")
 
 
 class PoolError(RuntimeError):
@@ -56,7 +58,12 @@ def load_host():
         "pa_pool_commit": (ctypes.c_int, [P, I64, I64]),
         "pa_pool_free_request": (ctypes.c_int, [P, I64, I32]),
         "pa_pool_fork": (ctypes.c_int, [P, I64, I64]),
-        "pa_pool_take_copies": (I64, [P, PI32, I64]),
+        "pa_pool_take_ops": (I64, [P, PI32, I64]),
+        "pa_pool_create_with_swap": (P, [I64, I64, I32]),
+        "pa_pool_swap_out": (ctypes.c_int, [P, I64]),
+        "pa_pool_swap_in": (ctypes.c_int, [P, I64]),
+        "pa_pool_request_swapped": (I32, [P, I64]),
+        "pa_pool_num_free_host_blocks": (I64, [P]),
         "pa_pool_num_blocks": (I64, [P]),
         "pa_pool_num_free_blocks": (I64, [P]),
         "pa_pool_num_cached_blocks": (I64, [P]),
@@ -94,9 +101,10 @@ def _check(status: int, call: str) -> int:
 class BlockPool:
     """Owns one pa_block_pool; methods mirror pa_pool_* (see include/pa_pool.h)."""
 
-    def __init__(self, num_blocks: int, prefix_caching: bool = True):
+    def __init__(self, num_blocks: int, prefix_caching: bool = True, num_host_blocks: int = 0):
         self._lib = load_host()
-        self._p = self._lib.pa_pool_create(int(num_blocks), int(bool(prefix_caching)))
+        self._p = self._lib.pa_pool_create_with_swap(int(num_blocks), int(num_host_blocks),
+                                                      int(bool(prefix_caching)))
         if not self._p:
             raise PoolError(-1, "pa_pool_create")
 
@@ -143,12 +151,27 @@ class BlockPool:
     def fork(self, parent_id: int, child_id: int) -> None:
         _check(self._lib.pa_pool_fork(self._p, parent_id, child_id), "pa_pool_fork")
 
-    def take_copies(self):
+    def swap_out(self, req_id: int) -> bool:
+        """False when the swap space is short (nothing changed)."""
+        return _check(self._lib.pa_pool_swap_out(self._p, req_id), "pa_pool_swap_out") == POOL_OK
+
+    def swap_in(self, req_id: int) -> bool:
+        """False when the free queue is short (nothing changed)."""
+        return _check(self._lib.pa_pool_swap_in(self._p, req_id), "pa_pool_swap_in") == POOL_OK
+
+    def request_swapped(self, req_id: int) -> bool:
+        return bool(_check(self._lib.pa_pool_request_swapped(self._p, req_id), "pa_pool_request_swapped"))
+
+    def num_free_host_blocks(self) -> int:
+        return self._lib.pa_pool_num_free_host_blocks(self._p)
+
+    def take_ops(self):
+        """Pending block operations, oldest first: list of (kind, source, destination)."""
         out = []
-        buf = np.empty(2 * 256, dtype=np.int32)
+        buf = np.empty(3 * 256, dtype=np.int32)
         while True:
-            n = _check(self._lib.pa_pool_take_copies(self._p, _p32(buf), 256), "pa_pool_take_copies")
-            out += [(int(buf[2 * i]), int(buf[2 * i + 1])) for i in range(n)]
+            n = _check(self._lib.pa_pool_take_ops(self._p, _p32(buf), 256), "pa_pool_take_ops")
+            out += [(int(buf[3 * i]), int(buf[3 * i + 1]), int(buf[3 * i + 2])) for i in range(n)]
             if n < 256:
                 return out
 
@@ -194,17 +217,20 @@ class BlockPool:
 # ----------------------------------------------------------------------------- scheduler
 SCHED_FCFS = 0
 SCHED_PRIORITY = 1
+SCHED_RECOMPUTE = 0
+SCHED_SWAP = 1
 
 SCHED_EXPORTED = ("pa_sched_create", "pa_sched_destroy", "pa_sched_add_request", "pa_sched_schedule",
                   "pa_sched_plan", "pa_sched_plan_tokens", "pa_sched_plan_prefills",
                   "pa_sched_plan_max_blocks", "pa_sched_batch", "pa_sched_update",
                   "pa_sched_num_waiting", "pa_sched_num_running", "pa_sched_num_preemptions",
-                  "pa_sched_take_finished", "pa_sched_last_error")
+                  "pa_sched_take_finished", "pa_sched_last_error", "pa_sched_num_swaps")
 
 
 class SchedConfig(ctypes.Structure):
     _fields_ = [("max_num_batched_tokens", ctypes.c_int32), ("max_num_seqs", ctypes.c_int32),
-                ("policy", ctypes.c_int32), ("chunked_prefill", ctypes.c_int32)]
+                ("policy", ctypes.c_int32), ("chunked_prefill", ctypes.c_int32),
+                ("preempt_mode", ctypes.c_int32)]
 
 
 def _load_sched(lib):
@@ -226,6 +252,7 @@ def _load_sched(lib):
         "pa_sched_num_waiting": (I64, [P]),
         "pa_sched_num_running": (I64, [P]),
         "pa_sched_num_preemptions": (I64, [P]),
+        "pa_sched_num_swaps": (I64, [P]),
         "pa_sched_take_finished": (I64, [P, PI64, I64]),
         "pa_sched_last_error": (ctypes.c_char_p, []),
     }
@@ -267,10 +294,11 @@ class Scheduler:
     """Owns one pa_scheduler over a BlockPool; methods mirror pa_sched_* (include/pa_sched.h)."""
 
     def __init__(self, pool: BlockPool, max_num_batched_tokens: int, max_num_seqs: int,
-                 policy: int = SCHED_FCFS, chunked_prefill: bool = True):
+                 policy: int = SCHED_FCFS, chunked_prefill: bool = True, preempt_mode: int = SCHED_RECOMPUTE):
         self._lib = _load_sched(load_host())
         self.pool = pool  # kept alive as long as the scheduler
-        cfg = SchedConfig(max_num_batched_tokens, max_num_seqs, policy, int(bool(chunked_prefill)))
+        cfg = SchedConfig(max_num_batched_tokens, max_num_seqs, policy, int(bool(chunked_prefill)),
+                          preempt_mode)
         self._s = self._lib.pa_sched_create(pool.handle, ctypes.byref(cfg))
         if not self._s:
             raise SchedError(-1, "pa_sched_create")
@@ -328,6 +356,9 @@ class Scheduler:
 
     def num_preemptions(self) -> int:
         return self._lib.pa_sched_num_preemptions(self._s)
+
+    def num_swaps(self) -> int:
+        return self._lib.pa_sched_num_swaps(self._s)
 
     def take_finished(self):
         buf = np.zeros(4096, dtype=np.int64)

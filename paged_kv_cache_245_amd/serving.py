@@ -2,12 +2,15 @@
 
 A step (arcyou teardown of vLLM paged attention, "Continuous batching: rebuild
 the batch every step") mixes prompt chunks and single generated tokens. Given
-the batch that libpa_host.so's scheduler planned (host.Scheduler.schedule), this
-module moves its metadata to the GPU in one copy and issues, on one stream:
-pa_copy_blocks for pending copy-on-write pairs, pa_write_kv for every new
-token's K/V, pa_prefill_chunk for the requests given more than one token, and
-pa_decode for the ones given exactly one. Marshalling and sequencing only; the
-work runs in libpa.so's kernels.
+the batch that libpa_host.so's scheduler planned (host.Scheduler.schedule) and
+the block operations the pool queued for it (host.BlockPool.take_ops), this
+module issues, on one stream: the block operations in their order
+(pa_copy_blocks for copy-on-write copies, pa_swap_blocks for swap-outs and
+swap-ins, consecutive operations of one kind batched into one call when none
+writes a block another reads or writes), one copy of the step's metadata to
+the GPU, pa_write_kv for every new token's K/V, pa_prefill_chunk for the
+requests given more than one token, and pa_decode for the ones given exactly
+one. Marshalling and sequencing only; the work runs in libpa.so's kernels.
 """
 from __future__ import annotations
 
@@ -15,6 +18,27 @@ import numpy as np
 import torch
 
 from . import _lib as pa
+from .host import OP_COPY, OP_SWAP_IN, OP_SWAP_OUT
+
+
+def batch_ops(ops):
+    """Split ordered block operations into runs of one kind that may execute as one call:
+    a run ends where an operation would write a block that the run already reads or
+    writes, or read a block that the run writes. Returns [(kind, [(src, dst), ...])]."""
+    runs = []
+    for kind, src, dst in ops:
+        # a block is named by (memory, id); copies live on the device, swaps cross to the host
+        s_mem, d_mem = {OP_COPY: ("d", "d"), OP_SWAP_OUT: ("d", "h"), OP_SWAP_IN: ("h", "d")}[kind]
+        s_key, d_key = (s_mem, src), (d_mem, dst)
+        if runs and runs[-1][0] == kind:
+            reads, writes = runs[-1][2], runs[-1][3]
+            if d_key not in reads and d_key not in writes and s_key not in writes:
+                runs[-1][1].append((src, dst))
+                reads.add(s_key)
+                writes.add(d_key)
+                continue
+        runs.append([kind, [(src, dst)], {s_key}, {d_key}])
+    return [(kind, pairs) for kind, pairs, _, _ in runs]
 
 
 class StepRunner:
@@ -26,8 +50,10 @@ class StepRunner:
     """
 
     def __init__(self, desc, k_cache, v_cache, scale, max_seqs, max_tokens, max_blocks_per_seq,
-                 device="cuda"):
+                 device="cuda", host_k=None, host_v=None):
+        """host_k/host_v: the pinned CPU swap space [num_host_blocks, 16, Hkv, D], if any."""
         self.desc, self.k, self.v, self.scale = desc, k_cache, v_cache, float(scale)
+        self.host_k, self.host_v = host_k, host_v
         self.max_seqs, self.max_tokens, self.max_blocks = max_seqs, max_tokens, max_blocks_per_seq
         self.device = torch.device(device)
         # room for one step's metadata (int32): qsl | seq_lens | tables | slots
@@ -39,8 +65,22 @@ class StepRunner:
         self.ws = pa.decode_workspace(desc, max_seqs, max_blocks_per_seq * 16, 0, self.device)
         self.ws_bytes = 0 if self.ws is None else self.ws.numel()
 
-    def run(self, batch, q, key, value, out, copies=()):
-        """q/out [N, Hq, D], key/value [N, Hkv, D]: the step's new tokens in batch order."""
+    def run_ops(self, ops):
+        """The pool's block operations (kind, source, destination), in order."""
+        for kind, pairs in batch_ops(ops):
+            t = torch.tensor(np.asarray(pairs, dtype=np.int32).reshape(-1, 2), device=self.device)
+            if kind == OP_COPY:
+                pa.pa_copy_blocks(self.desc, self.k, self.v, t)
+            else:
+                if self.host_k is None:
+                    raise ValueError("swap operations need the host swap space")
+                pa.pa_swap_blocks(self.desc, self.k, self.v, self.host_k, self.host_v, t,
+                                  pa.PA_SWAP_OUT if kind == OP_SWAP_OUT else pa.PA_SWAP_IN)
+
+    def run(self, batch, q, key, value, out, ops=()):
+        """q/out [N, Hq, D], key/value [N, Hkv, D]: the step's new tokens in batch order;
+        ops: the block operations the pool queued while the step was planned."""
+        self.run_ops(ops)
         S, N, P = batch.num_seqs, batch.num_tokens, batch.num_prefills
         if S == 0:
             return
@@ -48,9 +88,6 @@ class StepRunner:
         if S > self.max_seqs or N > self.max_tokens or mb > self.max_blocks:
             raise ValueError("step larger than the buffers of this StepRunner")
         stream = torch.cuda.current_stream(self.device)
-        if copies:
-            pairs = torch.tensor(np.asarray(copies, dtype=np.int32).reshape(-1, 2), device=self.device)
-            pa.pa_copy_blocks(self.desc, self.k, self.v, pairs)
 
         # pack the metadata (qsl | seq_lens | tables | slots) into the next pinned buffer,
         # then one host-to-device copy of the used length

@@ -4,7 +4,8 @@ Random sequences of calls (new requests with shared prompt pieces, chunked
 allocations, commits, generated tokens, forks, preemptions, finishes) run on
 both; after every call the results must be identical: return values, prefix
 hits, every block table, every reference count, the free queue in order, the
-cached-block count and the copy-on-write pairs. Integer work: exact equality.
+cached-block count, swap state and the ordered block operations (copy-on-write
+copies, swap-outs, swap-ins). Integer work: exact equality.
 """
 import random
 
@@ -26,17 +27,20 @@ def same_state(lib: host.BlockPool, model: bp.BlockPoolModel):
     assert lib.num_free_blocks() == len(model.free)
     assert [lib.ref_count(b) for b in range(len(model.ref))] == model.ref
     assert lib.num_cached_blocks() == model.num_cached()
+    assert lib.num_free_host_blocks() == len(model.host_free)
+    assert lib.take_ops() == model.take_ops()
     for rid, r in model.reqs.items():
+        assert lib.request_swapped(rid) == r.swapped
         assert lib.block_table(rid) == r.blocks, rid
         assert lib.request_computed(rid) == r.computed
         assert lib.request_tokens(rid) == len(r.tokens)
         assert lib.prefix_hit_tokens(rid) == model.prefix_hit_tokens(rid)
 
 
-def random_session(seed, num_blocks, prefix, steps=150):
+def random_session(seed, num_blocks, prefix, steps=150, num_host=0):
     rng = random.Random(seed)
-    lib = host.BlockPool(num_blocks, prefix)
-    model = bp.BlockPoolModel(num_blocks, prefix)
+    lib = host.BlockPool(num_blocks, prefix, num_host)
+    model = bp.BlockPoolModel(num_blocks, prefix, num_host)
     pieces = [[rng.randint(0, 50) for _ in range(B)] for _ in range(4)]
     next_id = 0
     for _ in range(steps):
@@ -52,18 +56,21 @@ def random_session(seed, num_blocks, prefix, steps=150):
         elif op < 0.5:
             rid = rng.choice(live)
             r = model.reqs[rid]
-            left = len(r.tokens) - r.computed - model.prefix_hit_tokens(rid)
-            n = rng.randint(0, max(left, 0))
-            got, want = lib.allocate_slots(rid, n), model.allocate_slots(rid, n)
-            assert got == want
-            assert lib.take_copies() == model.take_copies()
+            if r.swapped:
+                assert lib.swap_in(rid) == model.swap_in(rid)
+            else:
+                left = len(r.tokens) - r.computed - model.prefix_hit_tokens(rid)
+                n = rng.randint(0, max(left, 0))
+                got, want = lib.allocate_slots(rid, n), model.allocate_slots(rid, n)
+                assert got == want
         elif op < 0.65:
             rid = rng.choice(live)
             r = model.reqs[rid]
-            cover = min(B * len(r.blocks), len(r.tokens))
-            c = rng.randint(r.computed, cover)
-            lib.commit(rid, c)
-            model.commit(rid, c)
+            if not r.swapped:
+                cover = min(B * len(r.blocks), len(r.tokens))
+                c = rng.randint(r.computed, cover)
+                lib.commit(rid, c)
+                model.commit(rid, c)
         elif op < 0.72:
             rid = rng.choice(live)
             extra = [rng.randint(0, 60) for _ in range(rng.randint(1, 3))]
@@ -71,9 +78,16 @@ def random_session(seed, num_blocks, prefix, steps=150):
             model.append_tokens(rid, extra)
         elif op < 0.8:
             rid = rng.choice(live)
-            lib.fork(rid, next_id)
-            model.fork(rid, next_id)
-            next_id += 1
+            if not model.reqs[rid].swapped:
+                lib.fork(rid, next_id)
+                model.fork(rid, next_id)
+                next_id += 1
+        elif op < 0.88 and num_host:
+            rid = rng.choice(live)
+            if model.reqs[rid].swapped:
+                assert lib.swap_in(rid) == model.swap_in(rid)
+            else:
+                assert lib.swap_out(rid) == model.swap_out(rid)
         else:
             rid = rng.choice(live)
             keep = rng.random() < 0.5
@@ -93,6 +107,12 @@ def random_session(seed, num_blocks, prefix, steps=150):
 def test_matches_model(prefix, num_blocks):
     for seed in range(25):
         random_session(seed * 7 + num_blocks, num_blocks, prefix)
+
+
+@pytest.mark.parametrize("num_blocks,num_host", [(6, 3), (12, 12), (40, 8)])
+def test_matches_model_with_swap(num_blocks, num_host):
+    for seed in range(25):
+        random_session(seed * 11 + num_host, num_blocks, True, num_host=num_host)
 
 
 def test_chained_hash_depends_on_prefix_and_salt():
@@ -135,6 +155,28 @@ def test_errors_change_nothing():
     assert lib.ref_count(-1) == -1 and lib.ref_count(4) == -1
     with pytest.raises(host.PoolError):
         host.BlockPool(0)
+
+
+def test_swap_errors():
+    lib = host.BlockPool(8, True, 2)
+    lib.add_request(1, list(range(40)))
+    assert lib.allocate_slots(1, 40) == 0
+    lib.commit(1, 40)
+    assert lib.swap_out(1) is False               # needs 3 host blocks, has 2
+    assert lib.block_table(1) and not lib.request_swapped(1)
+    lib.add_request(2, list(range(100, 120)))
+    assert lib.allocate_slots(2, 20) == 0
+    lib.commit(2, 17)
+    assert lib.swap_out(2) is True and lib.request_swapped(2)
+    with pytest.raises(host.PoolError):
+        lib.allocate_slots(2, 1)                  # swapped: swap it in first
+    with pytest.raises(host.PoolError):
+        lib.fork(2, 3)
+    with pytest.raises(host.PoolError):
+        lib.swap_out(2)                           # already swapped
+    assert lib.swap_in(2) is True and lib.request_computed(2) == 17
+    with pytest.raises(host.PoolError):
+        lib.swap_in(2)                            # not swapped
 
 
 def test_exported_symbols():

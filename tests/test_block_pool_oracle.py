@@ -22,18 +22,26 @@ def tokens(n, base=0):
     return [base + i for i in range(n)]
 
 
-def run_chunk(pool, rid, n, device):
-    """Schedule n tokens of rid: allocate, apply copy-on-write copies, write, commit."""
+def apply_ops(ops, device, host=None):
+    """Run block operations in order on the simulated device (and host) contents."""
+    host = {} if host is None else host
+    for kind, src, dst in ops:
+        a, b = {bp.OP_COPY: (device, device), bp.OP_SWAP_OUT: (device, host),
+                bp.OP_SWAP_IN: (host, device)}[kind]
+        for o in range(B):
+            if src * B + o in a:
+                b[dst * B + o] = a[src * B + o]
+            else:
+                b.pop(dst * B + o, None)
+
+
+def run_chunk(pool, rid, n, device, host=None):
+    """Schedule n tokens of rid: allocate, run the queued block operations, write, commit."""
     r = pool.reqs[rid]
     hit = pool.allocate_slots(rid, n)
     if hit is None:
         return None
-    for src, dst in pool.take_copies():
-        for o in range(B):
-            if src * B + o in device:
-                device[dst * B + o] = device[src * B + o]
-            else:
-                device.pop(dst * B + o, None)
+    apply_ops(pool.take_ops(), device, host)
     start = r.computed
     for p, slot in zip(range(start, start + n), pool.slot_mapping(rid, start, n)):
         device[slot] = r.tokens[p]
@@ -41,9 +49,10 @@ def run_chunk(pool, rid, n, device):
     return hit
 
 
-def readback(pool, rid, device):
+def readback(pool, rid, device, host=None):
     r = pool.reqs[rid]
-    return [device.get(r.blocks[p // B] * B + p % B) for p in range(r.computed)]
+    where, blocks = (host, r.host_blocks) if r.swapped else (device, r.blocks)
+    return [where.get(blocks[p // B] * B + p % B) for p in range(r.computed)]
 
 
 # ----------------------------------------------------------------------------- pins
@@ -170,12 +179,38 @@ def pin_no_caching_when_disabled():
     assert pool.prefix_hit_tokens(2) == 0 and pool.num_cached() == 0
 
 
+def pin_swap_keeps_the_computed_tokens():
+    pool = bp.BlockPoolModel(8, True, num_host_blocks=3)
+    dev, hst = {}, {}
+    pool.add_request(1, tokens(45))
+    run_chunk(pool, 1, 37, dev)
+    t = pool.block_table(1)
+    assert pool.swap_out(1) is True
+    ops = pool.take_ops()
+    assert ops == [(bp.OP_SWAP_OUT, t[0], 0), (bp.OP_SWAP_OUT, t[1], 1), (bp.OP_SWAP_OUT, t[2], 2)]
+    apply_ops(ops, dev, hst)
+    assert pool.reqs[1].swapped and pool.reqs[1].computed == 37 and len(pool.free) == 8
+    for b in t:                          # someone else overwrites the old blocks
+        for o in range(B):
+            dev[b * B + o] = -1
+    assert pool.swap_in(1) is True and pool.host_free == [0, 1, 2]
+    apply_ops(pool.take_ops(), dev, hst)
+    assert readback(pool, 1, dev) == tokens(37)
+    assert run_chunk(pool, 1, 8, dev) == 0
+    assert readback(pool, 1, dev) == tokens(45)
+    pool.add_request(2, tokens(70, 500))
+    run_chunk(pool, 2, 60, dev)
+    assert pool.swap_out(2) is False     # 4 blocks hold computed tokens, 3 host blocks
+    assert not pool.reqs[2].swapped and len(pool.reqs[2].blocks) == 4
+
+
 def pin_reads_back_own_tokens_under_random_use():
-    """Fork, diverge, preempt, finish at random: every request reads back its tokens."""
+    """Fork, diverge, preempt (recompute or swap), finish at random: every request reads
+    back its tokens, with copies and swaps run in the order the pool queued them."""
     for seed in range(30):
         rng = random.Random(seed)
-        pool = bp.BlockPoolModel(rng.choice([6, 10, 24]), True)
-        dev = {}
+        pool = bp.BlockPoolModel(rng.choice([6, 10, 24]), True, num_host_blocks=rng.choice([0, 4, 12]))
+        dev, hst = {}, {}
         next_id = 0
         vocab = [tokens(B, 0), tokens(B, 50), tokens(B, 90)]
         for _ in range(120):
@@ -189,29 +224,37 @@ def pin_reads_back_own_tokens_under_random_use():
             elif op < 0.55:
                 rid = rng.choice(live)
                 r = pool.reqs[rid]
+                if r.swapped:
+                    if pool.swap_in(rid):
+                        apply_ops(pool.take_ops(), dev, hst)
+                    continue
                 left = len(r.tokens) - r.computed - pool.prefix_hit_tokens(rid)
                 if left <= 0:
                     pool.append_tokens(rid, [rng.randint(2000, 2100)])
                     left = 1
-                run_chunk(pool, rid, rng.randint(1, left), dev)
+                run_chunk(pool, rid, rng.randint(1, left), dev, hst)
             elif op < 0.7:
                 rid = rng.choice(live)
-                if pool.reqs[rid].computed:
+                if pool.reqs[rid].computed and not pool.reqs[rid].swapped:
                     pool.fork(rid, next_id)
                     pool.append_tokens(next_id, [rng.randint(3000, 3100)])
                     pool.append_tokens(rid, [rng.randint(4000, 4100)])
                     next_id += 1
-            elif op < 0.85:
+            elif op < 0.8:
+                rid = rng.choice(live)
+                if not pool.reqs[rid].swapped and pool.swap_out(rid):
+                    apply_ops(pool.take_ops(), dev, hst)
+            elif op < 0.9:
                 pool.free_request(rng.choice(live), keep=rng.random() < 0.5)
             for rid in pool.reqs:
-                assert readback(pool, rid, dev) == pool.reqs[rid].tokens[:pool.reqs[rid].computed]
+                assert readback(pool, rid, dev, hst) == pool.reqs[rid].tokens[:pool.reqs[rid].computed]
             held = sum(pool.ref)
             assert held == sum(len(r.blocks) for r in pool.reqs.values())
             assert sorted(pool.free + [b for b in range(len(pool.ref)) if pool.ref[b]]) == \
                 list(range(len(pool.ref)))
 
 
-ALL_PINS = [pin_new_request_takes_ceil_blocks, pin_exhaustion_returns_none_and_changes_nothing,
+ALL_PINS = [pin_swap_keeps_the_computed_tokens, pin_new_request_takes_ceil_blocks, pin_exhaustion_returns_none_and_changes_nothing,
             pin_identical_prompts_share_blocks, pin_hash_covers_the_whole_prefix,
             pin_extra_key_separates, pin_block_returns_only_at_zero_refs,
             pin_cached_blocks_evicted_last_prefix_last, pin_preempted_request_gets_its_prefix_back,
@@ -231,6 +274,20 @@ def _partial_allocate(self, rid, n_new):
     return 0
 
 
+def _swap_out_without_ops(self, rid):
+    ok = _orig_swap_out(self, rid)
+    self.ops = [o for o in self.ops if o[0] != bp.OP_SWAP_OUT]
+    return ok
+
+
+def _swap_in_reversed(self, rid):
+    self.reqs[rid].host_blocks.reverse()
+    return _orig_swap_in(self, rid)
+
+
+_orig_swap_out = bp.BlockPoolModel.swap_out
+_orig_swap_in = bp.BlockPoolModel.swap_in
+
 MISTAKES = {
     "hash of the block alone": ("prefix_key", lambda self, r, i: (r.salt, tuple(r.tokens[B * i:B * (i + 1)]))),
     "extra key ignored": ("prefix_key", lambda self, r, i: tuple(r.tokens[:B * (i + 1)])),
@@ -240,6 +297,8 @@ MISTAKES = {
     "hit may cover the last token": ("max_hit_blocks", lambda self, r: len(r.tokens) // B),
     "no copy on write": ("needs_copy", lambda self, r, start, n: False),
     "partial allocation instead of None": ("allocate_slots", _partial_allocate),
+    "swap-out moves nothing": ("swap_out", _swap_out_without_ops),
+    "swap-in reverses the blocks": ("swap_in", _swap_in_reversed),
 }
 
 

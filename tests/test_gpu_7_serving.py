@@ -11,7 +11,9 @@ GPU pool must equal the mirror bit for bit, untouched (poisoned) slots included.
 Synthetic K/V/Q: a token's rows depend only on the cache salt and the tokens up
 to it (a rolling 64-bit hash picks rows of a seeded table), as a model's would,
 so a block found in the prefix cache holds exactly what the request would have
-computed, and a recomputed token writes identical K/V.
+computed, and a recomputed token writes identical K/V. With a swap space, the
+preempted requests' blocks go to pinned host memory and back (pa_swap_blocks),
+and the host swap space must match its mirror bit for bit as well.
 """
 import numpy as np
 import pytest
@@ -62,13 +64,17 @@ class Synth:
         return self.k[idx], self.v[idx], self.q[qidx]
 
 
-@pytest.mark.parametrize("num_blocks,budget,max_seqs,seed", [(40, 96, 8, 1), (24, 48, 6, 2), (200, 256, 16, 3)])
-def test_serving_trace_matches_oracle(num_blocks, budget, max_seqs, seed):
-    say(f"serving trace: blocks {num_blocks}, budget {budget}, max_seqs {max_seqs}, seed {seed}")
+@pytest.mark.parametrize("num_blocks,budget,max_seqs,seed,num_host",
+                         [(40, 96, 8, 1, 0), (24, 48, 6, 2, 0), (200, 256, 16, 3, 0), (40, 96, 8, 4, 24),
+                          (24, 48, 6, 5, 10)])
+def test_serving_trace_matches_oracle(num_blocks, budget, max_seqs, seed, num_host):
+    say(f"serving trace: blocks {num_blocks}, budget {budget}, max_seqs {max_seqs}, seed {seed}, "
+        f"swap space {num_host}")
     rng = np.random.default_rng(seed)
     synth = Synth(seed)
-    pool = host.BlockPool(num_blocks, True)
-    sched = host.Scheduler(pool, budget, max_seqs)
+    pool = host.BlockPool(num_blocks, True, num_host)
+    sched = host.Scheduler(pool, budget, max_seqs,
+                           preempt_mode=host.SCHED_SWAP if num_host else host.SCHED_RECOMPUTE)
     shared = rng.integers(0, 500, 40).tolist()
     tokens, salts = {}, {}
     for i in range(12):
@@ -83,14 +89,20 @@ def test_serving_trace_matches_oracle(num_blocks, budget, max_seqs, seed):
     k_gpu, v_gpu = poison.clone().view(torch.bfloat16), poison.clone().view(torch.bfloat16)
     k_host = oracle.empty_pool(num_blocks, HKV, D, "bf16", POISON_BITS["bf16"])
     v_host = k_host.copy()
-    runner = StepRunner(desc, k_gpu, v_gpu, 1 / np.sqrt(D), max_seqs, budget, num_blocks)
+    nh = max(num_host, 1)
+    swap_k = torch.zeros((nh, 16, HKV, D), dtype=torch.bfloat16, pin_memory=True)
+    swap_v = torch.zeros((nh, 16, HKV, D), dtype=torch.bfloat16, pin_memory=True)
+    swap_k_host = oracle.empty_pool(nh, HKV, D, "bf16", 0)
+    swap_v_host = swap_k_host.copy()
+    runner = StepRunner(desc, k_gpu, v_gpu, 1 / np.sqrt(D), max_seqs, budget, num_blocks,
+                        host_k=swap_k, host_v=swap_v)
     scale = 1 / np.sqrt(D)
     mx, rel = TOL["bf16"]
     steps = 0
     while sched.num_waiting() or sched.num_running():
         b = sched.schedule()
         assert b.num_seqs > 0, "scheduler stalled"
-        copies = pool.take_copies()
+        ops = pool.take_ops()
         parts = [synth.rows(tokens[int(r)], salts[int(r)], int(a), int(c))
                  for r, a, c in zip(b.req_ids, b.starts, b.counts)]
         key = np.concatenate([p[0] for p in parts])
@@ -98,11 +110,15 @@ def test_serving_trace_matches_oracle(num_blocks, budget, max_seqs, seed):
         q = np.concatenate([p[2] for p in parts])
         out = torch.empty((b.num_tokens, HQ, D), dtype=torch.bfloat16, device="cuda")
         runner.run(b, device_tensor(q, "bf16"), device_tensor(key, "bf16"), device_tensor(value, "bf16"),
-                   out, copies)
+                   out, ops)
         torch.cuda.synchronize()
 
-        if copies:
-            oracle.copy_blocks(k_host, v_host, np.asarray(copies))
+        for kind, a, b_ in ops:  # the same block operations, one by one, in order
+            if kind == host.OP_COPY:
+                oracle.copy_blocks(k_host, v_host, [[a, b_]])
+            else:
+                oracle.swap_blocks(k_host, v_host, swap_k_host, swap_v_host, [[a, b_]],
+                                   kind == host.OP_SWAP_OUT)
         oracle.write_kv(k_host, v_host, key, value, b.slot_mapping)
         P, n_pf = b.num_prefills, int(b.query_start_loc[-1])
         got = out.to(torch.float64).cpu().numpy()
@@ -123,8 +139,13 @@ def test_serving_trace_matches_oracle(num_blocks, budget, max_seqs, seed):
                 tokens[r].append(int(sampled[i]))
         steps += 1
         assert steps < 2000
-    say(f"  {steps} steps, {sched.num_preemptions()} preemptions")
+    say(f"  {steps} steps, {sched.num_preemptions()} preemptions, {sched.num_swaps()} by swapping")
     assert np.array_equal(host_bits(k_gpu), k_host) and np.array_equal(host_bits(v_gpu), v_host)
+    sk = swap_k.view(torch.int16).numpy().view(np.uint16)
+    sv = swap_v.view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(sk, swap_k_host) and np.array_equal(sv, swap_v_host)
     if num_blocks <= 40:
         assert sched.num_preemptions() > 0
+    if num_host:
+        assert sched.num_swaps() > 0
     del mx, rel

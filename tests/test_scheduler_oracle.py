@@ -18,12 +18,27 @@ from oracle import scheduler as sm
 B = bp.BLOCK
 
 
-def make(num_blocks, budget, max_seqs=64, policy=sm.FCFS, chunked=True, prefix=True):
-    return sm.SchedulerModel(bp.BlockPoolModel(num_blocks, prefix), budget, max_seqs, policy, chunked)
+def make(num_blocks, budget, max_seqs=64, policy=sm.FCFS, chunked=True, prefix=True, num_host=0):
+    return sm.SchedulerModel(bp.BlockPoolModel(num_blocks, prefix, num_host), budget, max_seqs, policy,
+                             chunked, sm.SWAP if num_host else sm.RECOMPUTE)
 
 
-def step(s, dev=None, rng=None, produced=None):
+def apply_ops(ops, dev, hst):
+    """Run the pool's block operations in order on simulated device and host contents."""
+    for kind, src, dst in ops:
+        a, b = {bp.OP_COPY: (dev, dev), bp.OP_SWAP_OUT: (dev, hst), bp.OP_SWAP_IN: (hst, dev)}[kind]
+        for o in range(B):
+            if src * B + o in a:
+                b[dst * B + o] = a[src * B + o]
+            else:
+                b.pop(dst * B + o, None)
+
+
+def step(s, dev=None, rng=None, produced=None, hst=None):
     plan = s.schedule()
+    ops = s.pool.take_ops()
+    if dev is not None:
+        apply_ops(ops, dev, {} if hst is None else hst)
     if produced is not None:
         for rid, start, n in plan:
             if start + n == len(s.pool.reqs[rid].tokens):
@@ -41,9 +56,10 @@ def step(s, dev=None, rng=None, produced=None):
     return plan
 
 
-def readback_ok(s, dev):
+def readback_ok(s, dev, hst=None):
     for rid, r in s.pool.reqs.items():
-        got = [dev.get(r.blocks[p // B] * B + p % B) for p in range(r.computed)]
+        where, blocks = (hst, r.host_blocks) if r.swapped else (dev, r.blocks)
+        got = [where.get(blocks[p // B] * B + p % B) for p in range(r.computed)]
         if got != r.tokens[:r.computed]:
             return False
     return True
@@ -113,6 +129,42 @@ def pin_priority_preempts_lowest_priority_latest_arrival():
     assert s.preemptions == 1 and s.running == [2] and s.waiting == [1]
 
 
+def pin_swap_mode_resumes_where_it_stopped():
+    """Same trace as the FCFS preemption pin, with a swap space: the victim keeps its computed
+    tokens in host memory and resumes from them, so it is never recomputed."""
+    s = make(6, 64, num_host=4)
+    s.add_request(1, list(range(40)), 30)
+    s.add_request(2, list(range(100, 140)), 30)
+    step(s)
+    for _ in range(30):
+        step(s)
+        if s.preemptions:
+            break
+    r2 = s.pool.reqs[2]
+    assert s.swaps == 1 and r2.swapped and r2.computed > 40 and s.waiting == [2]
+    computed = r2.computed
+    for _ in range(200):
+        plan = step(s)
+        mine = [x for x in plan if x[0] == 2]
+        if mine:
+            assert mine[0][1] == computed  # resumes at its computed count
+            break
+    else:
+        raise AssertionError("swapped request never resumed")
+
+
+def pin_swap_mode_without_room_recomputes():
+    s = make(6, 64, num_host=2)  # request 2 needs 3 host blocks
+    s.add_request(1, list(range(40)), 30)
+    s.add_request(2, list(range(100, 140)), 30)
+    step(s)
+    for _ in range(30):
+        step(s)
+        if s.preemptions:
+            break
+    assert s.preemptions == 1 and s.swaps == 0 and s.pool.reqs[2].computed == 0
+
+
 def pin_finished_requests_release_their_blocks():
     s = make(8, 64)
     s.add_request(1, list(range(30)), 1)
@@ -137,19 +189,19 @@ def pin_without_chunking_a_prompt_waits_for_room():
 
 
 def pin_trace_completes_and_reads_back():
-    for seed in range(12):
+    for seed in range(16):
         rng = random.Random(seed)
         s = make(rng.choice([8, 12, 40]), rng.choice([16, 48]), max_seqs=rng.choice([2, 8]),
-                 policy=rng.choice([sm.FCFS, sm.PRIORITY]))
-        dev, produced, max_new = {}, {}, {}
+                 policy=rng.choice([sm.FCFS, sm.PRIORITY]), num_host=rng.choice([0, 0, 3, 10]))
+        dev, hst, produced, max_new = {}, {}, {}, {}
         shared = [rng.randint(0, 9) for _ in range(32)]
         for i in range(10):
             prompt = (shared if rng.random() < 0.5 else []) + [rng.randint(0, 9) for _ in range(rng.randint(1, 40))]
             max_new[i] = rng.randint(1, 8)
             s.add_request(i, prompt, max_new[i], priority=rng.randint(0, 2))
         for _ in range(2000):
-            step(s, dev, rng, produced)
-            assert readback_ok(s, dev)
+            step(s, dev, rng, produced, hst)
+            assert readback_ok(s, dev, hst)
             if not s.running and not s.waiting:
                 break
         assert sorted(s.finished) == list(range(10))
@@ -161,6 +213,7 @@ ALL_PINS = [pin_chunked_prefill_splits_a_long_prompt, pin_steps_mix_prompts_and_
             pin_preemption_takes_the_newest_and_requeues_it_first,
             pin_priority_preempts_lowest_priority_latest_arrival,
             pin_finished_requests_release_their_blocks, pin_no_admission_beyond_max_seqs,
+            pin_swap_mode_resumes_where_it_stopped, pin_swap_mode_without_room_recomputes,
             pin_without_chunking_a_prompt_waits_for_room, pin_trace_completes_and_reads_back]
 
 
@@ -200,12 +253,18 @@ def _keep_finished_blocks(self, sampled):
         self.pool.free_request = free
 
 
+def _swap_ignored(self):
+    self.preempt_mode = sm.RECOMPUTE
+    return _orig_schedule(self)
+
+
 _orig_schedule = sm.SchedulerModel.schedule
 _orig_update = sm.SchedulerModel.update
 MISTAKES.update({
     "decodes lead the batch": ("schedule", _plan_order_decodes_first),
     "whole prompts ignore the budget": ("schedule", _no_chunking),
     "finished requests keep their blocks": ("update", _keep_finished_blocks),
+    "swap mode recomputes instead": ("schedule", _swap_ignored),
 })
 
 
