@@ -66,6 +66,102 @@ __device__ __forceinline__ int v_phys(int row, int ch) {
   else return ch ^ (4 * ((row >> 1) & 1));
 }
 
+// Work items are (request, kv head, query tile); an item's cost is the number
+// of 64-key tiles it reads, ceil((cached + min((tile + 1) kPos, nq)) / 64). The
+// launch runs items heaviest first (longest-processing-time order): workgroup
+// number i (in dispatch order) takes the item of rank i in non-increasing cost,
+// ties broken by (request, query tile, kv head). Each workgroup finds its item
+// itself from the requests' lengths: a binary search on the cost level c with
+// count(c) = items of cost >= c, which is closed-form per request because cost
+// grows with the query tile.
+struct ReqShape {
+  int nq, cached, tiles;  // rows of the chunk, cached keys, query tiles (0: no work)
+};
+
+__device__ __forceinline__ ReqShape req_shape(const PrefillArgs& a, int r, int kPos) {
+  ReqShape q{0, 0, 0};
+  const int q0 = a.query_start_loc[r];
+  int nq = a.query_start_loc[r + 1] - q0;
+  int L = a.seq_lens[r];
+  nq = min(nq, a.max_query_len);
+  nq = min(nq, a.num_tokens - q0);
+  L = min(L, a.max_seq_len);
+  L = min(L, a.max_blocks * 16);
+  if (q0 < 0 || nq <= 0) return q;
+  q.nq = nq;
+  q.cached = max(L - nq, 0);
+  q.tiles = (nq + kPos - 1) / kPos;
+  return q;
+}
+
+// First query tile of a request whose cost is >= c (tiles when there is none).
+__device__ __forceinline__ int first_tile_ge(const ReqShape& q, int c, int kPos) {
+  const int64_t rest = 64LL * (c - 1) - q.cached;
+  if (rest < 0) return 0;
+  if (q.nq <= rest) return q.tiles;
+  return (int)min<int64_t>(rest / kPos, q.tiles);
+}
+
+__device__ __forceinline__ int64_t wave_sum_i64(int64_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Items of cost >= c over all requests (one wavefront, lanes over requests).
+__device__ int64_t items_cost_ge(const PrefillArgs& a, int c, int kPos, int lane) {
+  int64_t acc = 0;
+  for (int r = lane; r < a.num_seqs; r += 64) {
+    const ReqShape q = req_shape(a, r, kPos);
+    acc += (int64_t)a.num_kv_heads * (q.tiles - first_tile_ge(q, c, kPos));
+  }
+  return wave_sum_i64(acc);
+}
+
+// The item of rank `rank` in heaviest-first order, as (request, kv head, tile),
+// or request -1 when rank >= the number of items. Run by one whole wavefront;
+// every lane gets the result.
+__device__ void item_of_rank(const PrefillArgs& a, int64_t rank, int kPos, int lane, int out[3]) {
+  out[0] = -1;
+  out[1] = out[2] = 0;
+  if (items_cost_ge(a, 1, kPos, lane) <= rank) return;
+  int lo = 1, hi = (a.max_seq_len + 63) / 64 + 1;  // count(lo) > rank >= count(hi)
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (items_cost_ge(a, mid, kPos, lane) > rank) lo = mid;
+    else hi = mid;
+  }
+  const int c = lo;
+  const int64_t j = rank - items_cost_ge(a, c + 1, kPos, lane);  // rank among items of cost c
+  int64_t acc = 0;
+  for (int base = 0; base < a.num_seqs; base += 64) {
+    const int r = base + lane;
+    int64_t n = 0;
+    int f0 = 0;
+    if (r < a.num_seqs) {
+      const ReqShape q = req_shape(a, r, kPos);
+      f0 = first_tile_ge(q, c, kPos);
+      n = (int64_t)a.num_kv_heads * (first_tile_ge(q, c + 1, kPos) - f0);
+    }
+    int64_t incl = n;  // inclusive prefix sum over the lanes
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int64_t t = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += t;
+    }
+    const uint64_t hit = __ballot(r < a.num_seqs && j < acc + incl);
+    if (hit != 0) {
+      const int src = __ffsll((unsigned long long)hit) - 1;
+      const int64_t off = j - (acc + incl - n);  // meaningful on lane src
+      out[0] = __shfl(r, src, 64);
+      out[1] = __shfl((int)(off % a.num_kv_heads), src, 64);
+      out[2] = __shfl(f0 + (int)(off / a.num_kv_heads), src, 64);
+      return;
+    }
+    acc += __shfl(incl, 63, 64);
+  }
+}
+
 template <int D, int G>
 __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a) {
   static_assert(D == 64 || D == 128, "head_dim");
@@ -83,9 +179,21 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int Hkv = a.num_kv_heads;
-  const int kvh = blockIdx.x % Hkv;
-  const int s = blockIdx.x / Hkv;
-  const int tile = gridDim.y - 1 - blockIdx.y;
+  __shared__ int item[3];  // this workgroup's (request, kv head, query tile)
+  if (wave == 0) {
+    int mine[3];
+    item_of_rank(a, blockIdx.x + (int64_t)gridDim.x * blockIdx.y, kPos, lane, mine);
+    if (lane == 0) {
+      item[0] = mine[0];
+      item[1] = mine[1];
+      item[2] = mine[2];
+    }
+  }
+  __syncthreads();
+  const int s = item[0];
+  if (s < 0) return;  // uniform: more workgroups than items
+  const int kvh = item[1];
+  const int tile = item[2];
 
   const int q0 = a.query_start_loc[s];
   int nq = a.query_start_loc[s + 1] - q0;
