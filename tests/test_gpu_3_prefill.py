@@ -76,3 +76,16 @@ def test_empty_chunk_is_skipped():
     torch.cuda.synchronize()
     assert np.all(np.isfinite(as64(out[:5])))
     assert not out[5:].any()
+
+
+def test_many_requests_heaviest_first_order():
+    """150 chunks of mixed sizes: the in-kernel heaviest-first work order walks the requests
+    64 at a time, and every row must still be computed exactly once."""
+    rng = np.random.default_rng(81)
+    new = rng.integers(1, 41, 150)
+    new[::17] = 1
+    cached = rng.integers(0, 301, 150)
+    w = workloads.custom_prefill(81, cached=cached.tolist(), new=new.tolist(), Hq=8, Hkv=2, D=64,
+                                 dtype="bf16")
+    say(f"  150 requests, {int(new.sum())} rows")
+    check(w, "150 requests")
