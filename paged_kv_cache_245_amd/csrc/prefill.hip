@@ -35,6 +35,8 @@
 // Workgroups are ordered heaviest (last) query tile first; consecutive
 // workgroups take different kv heads of one request, so with 8 kv heads each
 // XCD's L2 serves one kv head's K/V to every query tile of that head.
+#include <type_traits>
+
 #include "pa_device.h"
 
 namespace pa {
@@ -308,10 +310,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
   __syncthreads();
   if (n_tiles > 1) stage_load(1);
 
-  for (int t = 0; t < n_tiles; ++t) {
-    const int buf = t & 1;
+  // one tile; the LDS stage is a compile-time constant so that operand
+  // addresses take it as an immediate offset
+  auto tile_step = [&](int t, auto stage) __attribute__((always_inline)) {
+    constexpr int buf = decltype(stage)::value;
     const int key0 = t * kBN;
-    const uint32_t koff = buf * kTileCh * 16u, voff = buf * kTileCh * 16u;
+    constexpr uint32_t koff = buf * kTileCh * 16u, voff = buf * kTileCh * 16u;
     f32x16 sacc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -417,6 +421,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
     if (t + 1 < n_tiles) stage_store(buf ^ 1);
     __syncthreads();
     if (t + 2 < n_tiles) stage_load(t + 2);
+  };
+  for (int t = 0; t < n_tiles; t += 2) {
+    tile_step(t, std::integral_constant<int, 0>{});
+    if (t + 1 < n_tiles) tile_step(t + 1, std::integral_constant<int, 1>{});
   }
 
   poisoned = __syncthreads_or(poisoned);
