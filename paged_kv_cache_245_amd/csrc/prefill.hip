@@ -32,9 +32,13 @@
 // Only tiles that cross the causal diagonal evaluate the mask.
 // Masked scores are set to -inf by selection; keys beyond the context are
 // staged as zeros, so no NaN from unused slots can reach the products.
-// Workgroups are ordered heaviest (last) query tile first; consecutive
-// workgroups take different kv heads of one request, so with 8 kv heads each
-// XCD's L2 serves one kv head's K/V to every query tile of that head.
+// The tile loop is unrolled by two, so the LDS stage of every operand read is an
+// immediate offset.
+// Work items (request, kv head, query tile) run heaviest first: workgroup i of
+// the dispatch order takes the item of rank i by cost (see item_of_rank).
+// Within one cost level consecutive workgroups take the kv heads of one
+// (request, tile) in turn, so with 8 kv heads each XCD (which receives every
+// 8th workgroup) keeps serving the same kv head's K/V from its L2.
 #include <type_traits>
 
 #include "pa_device.h"
