@@ -158,6 +158,26 @@ int pa_prefill_chunk(const pa_cache_desc* desc, void* out, const void* q,
                      int32_t max_blocks_per_seq, int32_t num_seqs, int32_t num_tokens,
                      int32_t max_query_len, int32_t max_seq_len, float scale, void* stream);
 
+/* Decode after appending each request's newest token: the same result as
+ * pa_write_kv of those tokens into their slots followed by pa_decode, in one
+ * kernel pass where the decode runs in its balanced bf16 mode (the default for
+ * bf16 pools, partition_tokens == 0), else as two launches. The newest token of
+ * request s sits at position context_lens[s] - 1 (context_lens counts it); its
+ * slot is read from the request's block table, so the block covering that
+ * position must be in the table (and, when shared, already copied on write).
+ * The kernel attends the newest key from `key`/`value` and the earlier keys
+ * from the pool, and stores the newest K/V into the pool for later steps
+ * (the KV cache grows one token at a time and every token re-reads all past
+ * K/V: arcyou teardown, "The problem both ideas solve"; kenhuang, "PagedAttention
+ * (intuition)").
+ *   key, value   [num_seqs][Hkv][D], pool dtype
+ * All other arguments, the workspace and the errors are those of pa_decode. */
+int pa_decode_append(const pa_cache_desc* desc, void* out, const void* q, const void* key,
+                     const void* value, void* k_cache, void* v_cache, const int32_t* block_tables,
+                     int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                     int32_t max_context_len, float scale, int32_t partition_tokens, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
 /* Copy whole blocks inside the pool, K and V alike: the copy-on-write step that
  * lets forked sequences share blocks until one of them must write into a shared
  * block, which is then duplicated first (aitrending, "The 1960s Operating System

@@ -21,6 +21,7 @@ from ._lib import (  # noqa: F401
     pa_bench_read,
     pa_copy_blocks,
     pa_decode,
+    pa_decode_append,
     pa_decode_partition_tokens,
     pa_decode_workspace_size,
     pa_gather_kv,

@@ -265,26 +265,74 @@ __device__ __forceinline__ void decode_segment(const DecodeArgs& a, int s, int k
     return id;
   };
   const LaneOffsets offs = lane_offsets<D>(kvh, Hkv, n, g4);
-  auto issue = [&](Tile<D>& t, int b) {
-    const bool two = b + 1 < blk_b;
-    const int32_t id0 = block_id(b);
-    const int32_t id1 = two ? block_id(b + 1) : 0;
-    load_pair<D, kNT>(t, K, V, id0, id1, two, offs);
-  };
 
-  end_tok = min(end_tok, 16 * blk_b);  // a segment may stop before the request does
-  Tile<D> ta, tb;
-  int b = blk_a;
-  issue(ta, b);
-  while (true) {
-    if (b + 2 < blk_b) issue(tb, b + 2);
-    attend_pair<D>(ta, qb, acc, m, lsum, a.scale_log2, min(32, end_tok - 16 * b), g4);
-    b += 2;
-    if (b >= blk_b) break;
-    if (b + 2 < blk_b) issue(ta, b + 2);
-    attend_pair<D>(tb, qb, acc, m, lsum, a.scale_log2, min(32, end_tok - 16 * b), g4);
-    b += 2;
-    if (b >= blk_b) break;
+  // In append mode the request's newest key (position end_tok - 1) comes from the
+  // input, not the pool: the pool is read up to it, and the segment holding it
+  // adds it last.
+  const bool append = a.new_k != nullptr;
+  const bool holds_newest = append && 16 * blk_b >= end_tok;
+  const int end_read = min(append ? end_tok - 1 : end_tok, 16 * blk_b);  // keys read from the pool
+  const int blk_r = min(blk_b, (end_read + 15) >> 4);                    // blocks holding them
+  if (blk_a < blk_r) {
+    auto issue_r = [&](Tile<D>& t, int bb) {
+      const bool two = bb + 1 < blk_r;
+      const int32_t id0 = block_id(bb);
+      const int32_t id1 = two ? block_id(bb + 1) : 0;
+      load_pair<D, kNT>(t, K, V, id0, id1, two, offs);
+    };
+    Tile<D> ta, tb;
+    int b = blk_a;
+    issue_r(ta, b);
+    while (true) {
+      if (b + 2 < blk_r) issue_r(tb, b + 2);
+      attend_pair<D>(ta, qb, acc, m, lsum, a.scale_log2, min(32, end_read - 16 * b), g4);
+      b += 2;
+      if (b >= blk_r) break;
+      if (b + 2 < blk_r) issue_r(ta, b + 2);
+      attend_pair<D>(tb, qb, acc, m, lsum, a.scale_log2, min(32, end_read - 16 * b), g4);
+      b += 2;
+      if (b >= blk_r) break;
+    }
+  }
+  if (holds_newest) {
+    // score of the newest key: lane (n, g4) holds q dims 32c + 8 g4 + 0..7
+    const int64_t nrow = ((int64_t)s * Hkv + kvh) * D;
+    const uint16_t* kn = (const uint16_t*)a.new_k + nrow;
+    const uint16_t* vn = (const uint16_t*)a.new_v + nrow;
+    float part = 0.f;
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+      const u32x4 kk = *(const u32x4*)(kn + 32 * c + 8 * g4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        part = __builtin_fmaf(bf16_bits_to_f32(qb[c][j] & 0xffffu), bf16_bits_to_f32(kk[j] & 0xffffu), part);
+        part = __builtin_fmaf(bf16_bits_to_f32(qb[c][j] >> 16), bf16_bits_to_f32(kk[j] >> 16), part);
+      }
+    }
+    part += __shfl_xor(part, 16, 64);
+    part += __shfl_xor(part, 32, 64);
+    const float sn = part * a.scale_log2;
+    const float m_new = fmaxf(m, sn);
+    const float alpha = fast_exp2(m - m_new);  // 0 when nothing came before
+    const float p = fast_exp2(sn - m_new);
+    lsum = lsum * alpha + (g4 == 0 ? p : 0.f);  // lanes of a head sum their partial l later
+    const float pr = bf16_bits_to_f32(f32_to_bf16_bits(p));  // P is bf16 in the products, too
+    // acc[d][i] of lane (n, g4) is dim (D/16) (4 g4 + i) + d
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint16_t* vrow = vn + kDL * (4 * g4 + i);
+#pragma unroll
+      for (int d = 0; d < kDL; ++d) acc[d][i] = __builtin_fmaf(pr, bf16_bits_to_f32(vrow[d]), acc[d][i] * alpha);
+    }
+    m = m_new;
+    // store the newest K/V into its slot: one wavefront per kv head, 16 bytes a lane
+    const int last = end_tok - 1;
+    const int32_t id = table[last >> 4];
+    if (block_ok(id, a.num_blocks) && lane < D / 8) {
+      const int64_t row = kv_row(id, last & 15, kvh, Hkv, D);
+      ((u32x4*)((uint16_t*)a.k + row))[lane] = ((const u32x4*)kn)[lane];
+      ((u32x4*)((uint16_t*)a.v + row))[lane] = ((const u32x4*)vn)[lane];
+    }
   }
 
   lsum += __shfl_xor(lsum, 16, 64);

@@ -229,11 +229,13 @@ size_t pa_decode_workspace_size(const pa_cache_desc* desc, int32_t num_seqs,
   return decode_layout(desc, num_seqs, max_context_len, partition_tokens).total;
 }
 
-int pa_decode(const pa_cache_desc* desc, void* out, const void* q, const void* k_cache,
-              const void* v_cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
-              const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
-              float scale, int32_t partition_tokens, void* workspace, size_t workspace_bytes,
-              void* stream) {
+namespace {
+// pa_decode, and pa_decode_append when new_k/new_v are given.
+int decode_impl(const pa_cache_desc* desc, void* out, const void* q, const void* new_k,
+                const void* new_v, const void* k_cache, const void* v_cache,
+                const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                int32_t num_seqs, int32_t max_context_len, float scale, int32_t partition_tokens,
+                void* workspace, size_t workspace_bytes, void* stream) {
   int st = validate_desc(desc);
   if (st != PA_OK) return st;
   if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs is negative");
@@ -241,6 +243,9 @@ int pa_decode(const pa_cache_desc* desc, void* out, const void* q, const void* k
   if (num_seqs > 65535) return fail(PA_ERR_UNSUPPORTED, "num_seqs above 65535");
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
     return fail(PA_ERR_INVALID_ARG, "null pointer argument");
+  const bool append = new_k != nullptr || new_v != nullptr;
+  if (append && (new_k == nullptr || new_v == nullptr))
+    return fail(PA_ERR_INVALID_ARG, "key and value of the newest tokens are both needed");
   if (max_blocks_per_seq <= 0) return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq must be positive");
   if (max_context_len <= 0) return fail(PA_ERR_INVALID_ARG, "max_context_len must be positive");
   if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * PA_BLOCK_SIZE)
@@ -287,8 +292,44 @@ int pa_decode(const pa_cache_desc* desc, void* out, const void* q, const void* k
   a.num_workers = lay.workers;
   a.nontemporal = nontemporal_mode(desc, num_seqs, max_context_len, lay.workers > 0);
   a.scale_log2 = scale * pa::kLog2e;
+  if (append) {
+    if (lay.workers > 0 && desc->dtype == PA_BF16) {
+      a.new_k = new_k;  // one pass: the balanced kernel attends and stores the newest token
+      a.new_v = new_v;
+    } else {
+      const int row_bytes = desc->num_kv_heads * desc->head_dim * elem_bytes(desc->dtype);
+      st = hip_status(pa::launch_append_kv(new_k, new_v, const_cast<void*>(k_cache), const_cast<void*>(v_cache),
+                                           block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                                           max_context_len, row_bytes, desc->num_blocks, as_stream(stream)),
+                      "append launch");
+      if (st != PA_OK) return st;
+    }
+  }
   return hip_status(pa::launch_decode(a, desc->head_dim, desc->dtype == PA_BF16, as_stream(stream)),
                     "decode launch");
+}
+}  // namespace
+
+int pa_decode(const pa_cache_desc* desc, void* out, const void* q, const void* k_cache,
+              const void* v_cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+              const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
+              float scale, int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+              void* stream) {
+  return decode_impl(desc, out, q, nullptr, nullptr, k_cache, v_cache, block_tables, max_blocks_per_seq,
+                     context_lens, num_seqs, max_context_len, scale, partition_tokens, workspace,
+                     workspace_bytes, stream);
+}
+
+int pa_decode_append(const pa_cache_desc* desc, void* out, const void* q, const void* key,
+                     const void* value, void* k_cache, void* v_cache, const int32_t* block_tables,
+                     int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                     int32_t max_context_len, float scale, int32_t partition_tokens, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  if (num_seqs > 0 && (key == nullptr || value == nullptr))
+    return fail(PA_ERR_INVALID_ARG, "null pointer argument");
+  return decode_impl(desc, out, q, key, value, k_cache, v_cache, block_tables, max_blocks_per_seq,
+                     context_lens, num_seqs, max_context_len, scale, partition_tokens, workspace,
+                     workspace_bytes, stream);
 }
 
 int pa_prefill_chunk(const pa_cache_desc* desc, void* out, const void* q, const void* k_cache,

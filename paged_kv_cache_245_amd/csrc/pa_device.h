@@ -95,6 +95,12 @@ struct DecodeArgs {
   int32_t nontemporal;       // stream K/V past the caches: 1 yes, 0 no, -1 kernel decides
   int32_t* cum_blocks;       // balanced mode: [S+1] prefix sums of blocks per request
   float scale_log2;  // scale * log2(e)
+  // Append mode (balanced bf16 only; both null otherwise): [S][Hkv][D] K and V of
+  // each request's newest token, position context_len - 1. The kernel attends it
+  // from here, reads only the keys before it from the pool, and stores it into
+  // its slot through the block table.
+  const void* new_k;
+  const void* new_v;
 };
 
 struct PrefillArgs {
@@ -120,6 +126,13 @@ hipError_t launch_write_kv(const void* key, const void* value, void* k_cache, vo
                            const int32_t* slots, int64_t num_tokens, int row_bytes,
                            int64_t num_slots, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, bool bf16, hipStream_t stream);
+// Stores each request's newest K/V row ([S][Hkv][D], position context_len - 1)
+// into its slot through the block table; requests with length < 1 or a bad
+// block id are skipped.
+hipError_t launch_append_kv(const void* key, const void* value, void* k_cache, void* v_cache,
+                            const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens,
+                            int32_t num_seqs, int32_t max_context_len, int row_bytes, int64_t num_blocks,
+                            hipStream_t stream);
 // kv heads handled by one decode workgroup (one wavefront each)
 int decode_waves(int num_kv_heads);
 // most requests the balanced decode mode accepts (block prefix sums live in LDS)

@@ -38,7 +38,40 @@ __global__ __launch_bounds__(256) void write_kv_kernel(const u32x4* __restrict__
   }
 }
 
+// Each request's newest token at position context_len - 1, stored through the
+// request's block table (one workgroup per request, 16-byte pieces of the row).
+__global__ __launch_bounds__(256) void append_kv_kernel(const u32x4* __restrict__ key,
+                                                        const u32x4* __restrict__ value,
+                                                        u32x4* __restrict__ k_cache,
+                                                        u32x4* __restrict__ v_cache,
+                                                        const int32_t* __restrict__ block_tables,
+                                                        int32_t max_blocks,
+                                                        const int32_t* __restrict__ context_lens,
+                                                        int32_t max_context_len, int pieces_per_row,
+                                                        int64_t num_blocks) {
+  const int s = blockIdx.x;
+  const int L = min(context_lens[s], max_context_len);
+  if (L < 1) return;
+  const int32_t id = block_tables[(int64_t)s * max_blocks + ((L - 1) >> 4)];
+  if (!block_ok(id, num_blocks)) return;
+  const int64_t dst = kv_row(id, (L - 1) & 15, 0, 1, pieces_per_row);
+  for (int i = threadIdx.x; i < pieces_per_row; i += blockDim.x) {
+    k_cache[dst + i] = key[(int64_t)s * pieces_per_row + i];
+    v_cache[dst + i] = value[(int64_t)s * pieces_per_row + i];
+  }
+}
+
 }  // namespace
+
+hipError_t launch_append_kv(const void* key, const void* value, void* k_cache, void* v_cache,
+                            const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens,
+                            int32_t num_seqs, int32_t max_context_len, int row_bytes, int64_t num_blocks,
+                            hipStream_t stream) {
+  hipLaunchKernelGGL(append_kv_kernel, dim3((unsigned)num_seqs), dim3(256), 0, stream, (const u32x4*)key,
+                     (const u32x4*)value, (u32x4*)k_cache, (u32x4*)v_cache, block_tables, max_blocks,
+                     context_lens, max_context_len, row_bytes / 16, num_blocks);
+  return hipGetLastError();
+}
 
 hipError_t launch_write_kv(const void* key, const void* value, void* k_cache, void* v_cache,
                            const int32_t* slots, int64_t num_tokens, int row_bytes,

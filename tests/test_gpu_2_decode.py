@@ -150,3 +150,55 @@ def test_balanced_relabelling_and_sharing_bit_identical():
     pn = perm.cpu().numpy()
     bt[bt >= 0] = pn[bt[bt >= 0]]
     assert np.array_equal(base, host_bits(run_decode(w, d, k2, v2, tables=bt)))
+
+
+def run_append(w, d, k, v, partition_tokens=0):
+    """pa_decode_append with the step's new tokens (one per decode request, in request order)."""
+    dec = w.decode
+    S = len(dec.context_lens)
+    sw = w.step_write
+    # the step writes exactly the newest token of every decode request, in request order
+    tbl, lens = dec.block_tables, dec.context_lens
+    expect = [int(tbl[s, (lens[s] - 1) // 16]) * 16 + (lens[s] - 1) % 16 for s in range(S)]
+    assert sw.slot_mapping.tolist() == expect
+    q = device_tensor(dec.q, w.spec.dtype)
+    out = torch.empty_like(q)
+    ws = pa.decode_workspace(d, S, dec.max_context_len, partition_tokens)
+    pa.pa_decode_append(d, out, q, device_tensor(sw.key, w.spec.dtype), device_tensor(sw.value, w.spec.dtype),
+                        k, v, i32(tbl), i32(lens), dec.max_context_len, w.scale, ws, partition_tokens)
+    torch.cuda.synchronize()
+    return out
+
+
+def check_append(w, partition_tokens=0, what=""):
+    """The fused call must leave the pools exactly as pa_write_kv would and match the oracle."""
+    d, k, v = gpu_pools(w, include_step=False)
+    out = run_append(w, d, k, v, partition_tokens)
+    ok, ov = oracle_pools(w)
+    view = (lambda a: a.view(np.uint32)) if w.spec.dtype == "f32" else (lambda a: a)
+    assert np.array_equal(view(host_bits(k)), view(ok)) and np.array_equal(view(host_bits(v)), view(ov))
+    assert_close(as64(out), oracle_decode(w, ok, ov), w.spec.dtype, what or f"append {w.name}")
+    return out
+
+
+@pytest.mark.parametrize("index", [1, 2, 3])
+def test_append_matches_write_then_decode(index):
+    say(f"  decode_append config {index}")
+    check_append(workloads.make(index))
+
+
+@pytest.mark.parametrize("part", [512, 48])
+def test_append_fixed_partitions(part):
+    check_append(workloads.c2_decode_batch(seed=9, num_seqs=12, len_lo=1, len_hi=1500), part,
+                 f"append partition {part}")
+
+
+@pytest.mark.parametrize("workers", [1, 5, 100000])
+def test_append_block_boundaries(workers, monkeypatch):
+    """Newest tokens that open a new block (length 1, 17, 33, ...), with workers down to one
+    block each, so some segments read no pool key at all and attend only the newest one."""
+    monkeypatch.setenv("PA_DECODE_WORKERS", str(workers))
+    w = workloads.custom_decode(19, [1, 17, 33, 16, 32, 100, 2, 49], Hq=8, Hkv=2, D=128, dtype="bf16")
+    out = check_append(w, 0, f"append workers {workers}")
+    # a context of one token returns that token's V exactly
+    assert np.array_equal(host_bits(out)[0], np.repeat(w.step_write.value[0], 4, axis=0))
