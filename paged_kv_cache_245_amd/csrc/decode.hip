@@ -265,74 +265,26 @@ __device__ __forceinline__ void decode_segment(const DecodeArgs& a, int s, int k
     return id;
   };
   const LaneOffsets offs = lane_offsets<D>(kvh, Hkv, n, g4);
+  auto issue = [&](Tile<D>& t, int b) {
+    const bool two = b + 1 < blk_b;
+    const int32_t id0 = block_id(b);
+    const int32_t id1 = two ? block_id(b + 1) : 0;
+    load_pair<D, kNT>(t, K, V, id0, id1, two, offs);
+  };
 
-  // In append mode the request's newest key (position end_tok - 1) comes from the
-  // input, not the pool: the pool is read up to it, and the segment holding it
-  // adds it last.
-  const bool append = a.new_k != nullptr;
-  const bool holds_newest = append && 16 * blk_b >= end_tok;
-  const int end_read = min(append ? end_tok - 1 : end_tok, 16 * blk_b);  // keys read from the pool
-  const int blk_r = min(blk_b, (end_read + 15) >> 4);                    // blocks holding them
-  if (blk_a < blk_r) {
-    auto issue_r = [&](Tile<D>& t, int bb) {
-      const bool two = bb + 1 < blk_r;
-      const int32_t id0 = block_id(bb);
-      const int32_t id1 = two ? block_id(bb + 1) : 0;
-      load_pair<D, kNT>(t, K, V, id0, id1, two, offs);
-    };
-    Tile<D> ta, tb;
-    int b = blk_a;
-    issue_r(ta, b);
-    while (true) {
-      if (b + 2 < blk_r) issue_r(tb, b + 2);
-      attend_pair<D>(ta, qb, acc, m, lsum, a.scale_log2, min(32, end_read - 16 * b), g4);
-      b += 2;
-      if (b >= blk_r) break;
-      if (b + 2 < blk_r) issue_r(ta, b + 2);
-      attend_pair<D>(tb, qb, acc, m, lsum, a.scale_log2, min(32, end_read - 16 * b), g4);
-      b += 2;
-      if (b >= blk_r) break;
-    }
-  }
-  if (holds_newest) {
-    // score of the newest key: lane (n, g4) holds q dims 32c + 8 g4 + 0..7
-    const int64_t nrow = ((int64_t)s * Hkv + kvh) * D;
-    const uint16_t* kn = (const uint16_t*)a.new_k + nrow;
-    const uint16_t* vn = (const uint16_t*)a.new_v + nrow;
-    float part = 0.f;
-#pragma unroll
-    for (int c = 0; c < kChunks; ++c) {
-      const u32x4 kk = *(const u32x4*)(kn + 32 * c + 8 * g4);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        part = __builtin_fmaf(bf16_bits_to_f32(qb[c][j] & 0xffffu), bf16_bits_to_f32(kk[j] & 0xffffu), part);
-        part = __builtin_fmaf(bf16_bits_to_f32(qb[c][j] >> 16), bf16_bits_to_f32(kk[j] >> 16), part);
-      }
-    }
-    part += __shfl_xor(part, 16, 64);
-    part += __shfl_xor(part, 32, 64);
-    const float sn = part * a.scale_log2;
-    const float m_new = fmaxf(m, sn);
-    const float alpha = fast_exp2(m - m_new);  // 0 when nothing came before
-    const float p = fast_exp2(sn - m_new);
-    lsum = lsum * alpha + (g4 == 0 ? p : 0.f);  // lanes of a head sum their partial l later
-    const float pr = bf16_bits_to_f32(f32_to_bf16_bits(p));  // P is bf16 in the products, too
-    // acc[d][i] of lane (n, g4) is dim (D/16) (4 g4 + i) + d
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint16_t* vrow = vn + kDL * (4 * g4 + i);
-#pragma unroll
-      for (int d = 0; d < kDL; ++d) acc[d][i] = __builtin_fmaf(pr, bf16_bits_to_f32(vrow[d]), acc[d][i] * alpha);
-    }
-    m = m_new;
-    // store the newest K/V into its slot: one wavefront per kv head, 16 bytes a lane
-    const int last = end_tok - 1;
-    const int32_t id = table[last >> 4];
-    if (block_ok(id, a.num_blocks) && lane < D / 8) {
-      const int64_t row = kv_row(id, last & 15, kvh, Hkv, D);
-      ((u32x4*)((uint16_t*)a.k + row))[lane] = ((const u32x4*)kn)[lane];
-      ((u32x4*)((uint16_t*)a.v + row))[lane] = ((const u32x4*)vn)[lane];
-    }
+  end_tok = min(end_tok, 16 * blk_b);  // a segment may stop before the request does
+  Tile<D> ta, tb;
+  int b = blk_a;
+  issue(ta, b);
+  while (true) {
+    if (b + 2 < blk_b) issue(tb, b + 2);
+    attend_pair<D>(ta, qb, acc, m, lsum, a.scale_log2, min(32, end_tok - 16 * b), g4);
+    b += 2;
+    if (b >= blk_b) break;
+    if (b + 2 < blk_b) issue(ta, b + 2);
+    attend_pair<D>(tb, qb, acc, m, lsum, a.scale_log2, min(32, end_tok - 16 * b), g4);
+    b += 2;
+    if (b >= blk_b) break;
   }
 
   lsum += __shfl_xor(lsum, 16, 64);
@@ -345,13 +297,24 @@ __device__ __forceinline__ void decode_segment(const DecodeArgs& a, int s, int k
     store_partial<D>(a, pidx_base + (int64_t)h * pidx_stride, acc, m, lsum, g4);
 }
 
-__device__ __forceinline__ int request_blocks(const DecodeArgs& a, int s) {
+// Keys of request s that the balanced kernel reads from the pool: all of its
+// context, or in append mode all but the newest token (the merge attends that one).
+template <bool kAppend>
+__device__ __forceinline__ int pool_keys(const DecodeArgs& a, int s) {
   const int L = min(a.context_lens[s], a.max_context_len);
-  return L > 0 ? (L + 15) >> 4 : 0;
+  return kAppend ? L - 1 : L;
+}
+
+template <bool kAppend>
+__device__ __forceinline__ int request_blocks(const DecodeArgs& a, int s) {
+  const int n = pool_keys<kAppend>(a, s);
+  return n > 0 ? (n + 15) >> 4 : 0;
 }
 
 // Balanced mode: grid (W, kv-head groups); dynamic LDS holds S+1 ints.
-template <int D, int NW>
+// kAppend: the pool is read up to each request's newest token and every segment
+// leaves a partial, which the merge combines with the newest key.
+template <int D, int NW, bool kAppend>
 __global__ __launch_bounds__(64 * NW) void decode_bf16_balanced_kernel(DecodeArgs a) {
   extern __shared__ int32_t cum[];
   __shared__ int32_t wave_total[NW];
@@ -365,7 +328,7 @@ __global__ __launch_bounds__(64 * NW) void decode_bf16_balanced_kernel(DecodeArg
   const int per = (S + kThreads - 1) / kThreads;
   const int r0 = min(tid * per, S), r1 = min(r0 + per, S);
   int mine = 0;
-  for (int r = r0; r < r1; ++r) mine += request_blocks(a, r);
+  for (int r = r0; r < r1; ++r) mine += request_blocks<kAppend>(a, r);
   int incl = mine;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -379,7 +342,7 @@ __global__ __launch_bounds__(64 * NW) void decode_bf16_balanced_kernel(DecodeArg
   int run = before + incl - mine;
   for (int r = r0; r < r1; ++r) {
     cum[r] = run;
-    run += request_blocks(a, r);
+    run += request_blocks<kAppend>(a, r);
   }
   if (tid == kThreads - 1) cum[S] = run;
   __syncthreads();
@@ -411,14 +374,14 @@ __global__ __launch_bounds__(64 * NW) void decode_bf16_balanced_kernel(DecodeArg
     const int ce = __builtin_amdgcn_readfirstlane(cum[s + 1]);
     if (ce > pos) {
       const int seg_end = min(ce, hi);
-      const int L = min(a.context_lens[s], a.max_context_len);
-      const bool whole = pos == cs && seg_end == ce;
+      const int n_keys = pool_keys<kAppend>(a, s);
+      const bool whole = !kAppend && pos == cs && seg_end == ce;
       const int64_t slot = (int64_t)s + w;
       if (nt)
-        decode_segment<D, true>(a, s, kvh, pos - cs, seg_end - cs, L, whole,
+        decode_segment<D, true>(a, s, kvh, pos - cs, seg_end - cs, n_keys, whole,
                                 slot * a.num_q_heads, 1);
       else
-        decode_segment<D, false>(a, s, kvh, pos - cs, seg_end - cs, L, whole,
+        decode_segment<D, false>(a, s, kvh, pos - cs, seg_end - cs, n_keys, whole,
                                  slot * a.num_q_heads, 1);
       pos = seg_end;
     }
@@ -432,18 +395,17 @@ __device__ __forceinline__ int worker_of(int64_t b, int64_t T, int W) {
   return (int)(((b + 1) * W + T - 1) / T) - 1;
 }
 
-// Balanced mode merge: one wavefront per (q head, request); lanes own D/64 dims.
 // Merge of split-KV partials (m, l, acc) of one (request, q head): partial i is
-// row row0 + i * rstep of the workspace. Returns o = sum_i 2^(m_i - M) acc_i and
-// den = sum_i 2^(m_i - M) l_i for M = max_i m_i; the caller divides.
+// row row0 + i * rstep of the workspace. Returns M = max_i m_i (-inf for none),
+// o = sum_i 2^(m_i - M) acc_i and den = sum_i 2^(m_i - M) l_i; the caller divides.
 // Partials are read eight at a time, all loads of a batch issued before any use,
 // and folded into a running (M, den, o) rescaled to the batch maximum.
 template <int D>
 __device__ __forceinline__ void fold_partials(const DecodeArgs& a, int64_t row0, int64_t rstep, int np,
-                                              int lane, float (&o)[D / 64], float& den) {
+                                              int lane, float (&o)[D / 64], float& den, float& M) {
   constexpr int kE = D / 64;
   constexpr int kBatch = 8;
-  float M = -INFINITY;
+  M = -INFINITY;
   den = 0.f;
 #pragma unroll
   for (int e = 0; e < kE; ++e) o[e] = 0.f;
@@ -477,7 +439,14 @@ __device__ __forceinline__ void fold_partials(const DecodeArgs& a, int64_t row0,
   }
 }
 
-template <int D>
+// Balanced mode merge, one wavefront per (q head, request); lanes own D/64 dims.
+// In append mode (kAppend) every request is merged here: its partials (none when
+// the newest token is its only one) and its newest key, read from a.new_k /
+// a.new_v and attended as one more partial with m = its score, l = 1 and acc =
+// its V row. The wavefront of the group's first q head also stores that K/V row
+// into the request's slot at position L - 1, after the decode kernel has read
+// the pool.
+template <int D, bool kAppend>
 __global__ __launch_bounds__(64) void decode_merge_balanced_kernel(DecodeArgs a) {
   constexpr int kE = D / 64;
   const int lane = threadIdx.x;
@@ -492,15 +461,54 @@ __global__ __launch_bounds__(64) void decode_merge_balanced_kernel(DecodeArgs a)
     return;
   }
   const int64_t T = a.cum_blocks[a.num_seqs];
-  const int W = (int)min((int64_t)a.num_workers, T);  // as in the decode kernel
-  const int w0 = worker_of(a.cum_blocks[s], T, W);
-  const int w1 = worker_of(a.cum_blocks[s + 1] - 1, T, W);
-  if (w0 == w1) return;  // one segment: written by the decode kernel
-  const int np = w1 - w0 + 1;
-  // partial of worker w0 + i for this (request, head) is row (s + w0 + i) * Hq + h
-  const int64_t row0 = ((int64_t)s + w0) * a.num_q_heads + h;
-  float o[kE], den;
-  fold_partials<D>(a, row0, a.num_q_heads, np, lane, o, den);
+  const int64_t c0 = a.cum_blocks[s], c1 = a.cum_blocks[s + 1];
+  int np = 0;
+  int64_t row0 = 0;
+  if (c1 > c0) {
+    const int W = (int)min((int64_t)a.num_workers, T);  // as in the decode kernel
+    const int w0 = worker_of(c0, T, W);
+    const int w1 = worker_of(c1 - 1, T, W);
+    if (!kAppend && w0 == w1) return;  // one segment: written by the decode kernel
+    np = w1 - w0 + 1;
+    // partial of worker w0 + i for this (request, head) is row (s + w0 + i) * Hq + h
+    row0 = ((int64_t)s + w0) * a.num_q_heads + h;
+  }
+  float o[kE], den, M;
+  fold_partials<D>(a, row0, a.num_q_heads, np, lane, o, den, M);
+  if constexpr (kAppend) {
+    const int kvh = h / a.group;
+    const int64_t nrow = ((int64_t)s * a.num_kv_heads + kvh) * D + kE * lane;
+    const uint16_t* qp = (const uint16_t*)a.q + orow;
+    const uint16_t* kp = (const uint16_t*)a.new_k + nrow;
+    const uint16_t* vp = (const uint16_t*)a.new_v + nrow;
+    uint32_t kb[kE], vb[kE];
+    float part = 0.f;
+#pragma unroll
+    for (int e = 0; e < kE; ++e) {
+      kb[e] = kp[e];
+      vb[e] = vp[e];
+      part = __builtin_fmaf(bf16_bits_to_f32(qp[e]), bf16_bits_to_f32(kb[e]), part);
+    }
+    const float sn = wave_sum(part) * a.scale_log2;  // the same value in every lane
+    const float mb = fmaxf(M, sn);
+    const float alpha = fast_exp2(M - mb);  // 0 when there is no partial
+    const float wn = fast_exp2(sn - mb);
+    den = den * alpha + wn;
+#pragma unroll
+    for (int e = 0; e < kE; ++e) o[e] = __builtin_fmaf(wn, bf16_bits_to_f32(vb[e]), o[e] * alpha);
+    const int last = L - 1;
+    const int32_t id = a.block_tables[(int64_t)s * a.max_blocks + (last >> 4)];
+    if (!block_ok(id, a.num_blocks)) {
+      den = __builtin_nanf("");  // as for any out-of-range block id
+    } else if (h % a.group == 0) {
+      const int64_t row = kv_row(id, last & 15, kvh, a.num_kv_heads, D) + kE * lane;
+#pragma unroll
+      for (int e = 0; e < kE; ++e) {
+        ((uint16_t*)a.k)[row + e] = (uint16_t)kb[e];
+        ((uint16_t*)a.v)[row + e] = (uint16_t)vb[e];
+      }
+    }
+  }
   const float inv = 1.f / den;
   if constexpr (kE == 2)
     *(uint32_t*)(O + orow) = pack_bf16x2(o[0] * inv, o[1] * inv);
@@ -671,7 +679,8 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   if (nparts <= 1) return;
   const int64_t base = ((int64_t)s * a.num_q_heads + h) * a.max_parts;
   float o[kE], den;
-  fold_partials<D>(a, base, 1, nparts, lane, o, den);
+  float M;
+  fold_partials<D>(a, base, 1, nparts, lane, o, den, M);
   const float inv = 1.f / den;
   const int64_t orow = ((int64_t)s * a.num_q_heads + h) * D + kE * lane;
   if constexpr (kBf16) {
@@ -699,8 +708,12 @@ void launch_bf16_nw(const DecodeArgs& a, hipStream_t stream) {
   if (a.num_workers > 0) {
     const int groups = (a.num_kv_heads + NW - 1) / NW;
     const size_t lds = sizeof(int32_t) * (size_t)(a.num_seqs + 1);
-    hipLaunchKernelGGL((decode_bf16_balanced_kernel<D, NW>), dim3(a.num_workers, groups),
-                       dim3(64 * NW), lds, stream, a);
+    if (a.new_k != nullptr)
+      hipLaunchKernelGGL((decode_bf16_balanced_kernel<D, NW, true>), dim3(a.num_workers, groups),
+                         dim3(64 * NW), lds, stream, a);
+    else
+      hipLaunchKernelGGL((decode_bf16_balanced_kernel<D, NW, false>), dim3(a.num_workers, groups),
+                         dim3(64 * NW), lds, stream, a);
   } else if (a.nontemporal > 0) {
     launch_grid<D, NW, true>(a, stream);
   } else {
@@ -725,7 +738,10 @@ hipError_t launch_decode_d(const DecodeArgs& a, bool bf16, hipStream_t stream) {
   if (e != hipSuccess) return e;
   dim3 mgrid(a.num_q_heads, a.num_seqs);
   if (a.num_workers > 0) {
-    hipLaunchKernelGGL(decode_merge_balanced_kernel<D>, mgrid, dim3(64), 0, stream, a);
+    if (a.new_k != nullptr)
+      hipLaunchKernelGGL((decode_merge_balanced_kernel<D, true>), mgrid, dim3(64), 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_merge_balanced_kernel<D, false>), mgrid, dim3(64), 0, stream, a);
   } else if (a.max_parts > 1) {
     if (bf16)
       hipLaunchKernelGGL((decode_merge_kernel<D, true>), mgrid, dim3(64), 0, stream, a);

@@ -96,9 +96,9 @@ struct DecodeArgs {
   int32_t* cum_blocks;       // balanced mode: [S+1] prefix sums of blocks per request
   float scale_log2;  // scale * log2(e)
   // Append mode (balanced bf16 only; both null otherwise): [S][Hkv][D] K and V of
-  // each request's newest token, position context_len - 1. The kernel attends it
-  // from here, reads only the keys before it from the pool, and stores it into
-  // its slot through the block table.
+  // each request's newest token, position context_len - 1. The decode kernel
+  // reads only the keys before it from the pool; the merge attends it from here
+  // and stores it into its slot through the block table.
   const void* new_k;
   const void* new_v;
 };

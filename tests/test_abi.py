@@ -98,6 +98,28 @@ def test_decode_argument_checks(lib):
     assert call_decode(lib, d, ws=ctypes.c_void_p(0x1000), ws_bytes=need - 1) == WORKSPACE
 
 
+def call_append(lib, d, key, value, **kw):
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+    a = dict(out=fake, q=fake, k=fake, v=fake, bt=fake, max_blocks=256, lens=fake, S=4,
+             max_ctx=4096, scale=0.088, part=0)
+    a.update(kw)
+    return lib.pa_decode_append(ctypes.byref(d), a["out"], a["q"], key, value, a["k"], a["v"], a["bt"],
+                                a["max_blocks"], a["lens"], a["S"], a["max_ctx"], a["scale"], a["part"],
+                                None, 0, None)
+
+
+def test_decode_append_argument_checks(lib):
+    d, fake = desc(), ctypes.c_void_p(0x1000)
+    assert call_append(lib, d, None, fake) == INVALID               # newest keys missing
+    assert call_append(lib, d, fake, None) == INVALID               # newest values missing
+    assert call_append(lib, d, fake, fake, out=None) == INVALID
+    assert call_append(lib, d, fake, fake, max_ctx=4097) == INVALID  # > 16 * max_blocks
+    assert call_append(lib, d, fake, fake, part=24) == INVALID
+    assert call_append(lib, d, fake, fake) == WORKSPACE              # same split rule as pa_decode
+    assert call_append(lib, d, None, None, S=0) == PA_OK            # empty batch: nothing to do
+    assert call_append(lib, desc(head_dim=96), fake, fake) == UNSUPPORTED
+
+
 def test_workspace_size_formula(lib):
     d = desc(num_q_heads=64)
     for S, L, P in ((8, 131072, 1024), (64, 4096, 512), (4, 100, 16)):
