@@ -35,8 +35,9 @@
  *     sampled token for it is appended; it finishes when it has produced
  *     max_new_tokens tokens (the last one is not appended).
  *
- * The step's batch is laid out for one pa_write_kv, one pa_prefill_chunk (the
- * requests given more than one token) and one pa_decode (those given one):
+ * The step's batch is laid out for one pa_write_kv and one pa_prefill_chunk (the
+ * requests given more than one token) and one pa_decode_append (those given
+ * one, whose new token is the newest of their context):
  * scheduled requests in batch order are the multi-token ones, then the
  * one-token ones, each group in scheduling order; new tokens are packed in the
  * same order. The block operations the step caused (swap-outs, swap-ins,

@@ -8,9 +8,10 @@ module issues, on one stream: the block operations in their order
 (pa_copy_blocks for copy-on-write copies, pa_swap_blocks for swap-outs and
 swap-ins, consecutive operations of one kind batched into one call when none
 writes a block another reads or writes), one copy of the step's metadata to
-the GPU, pa_write_kv for every new token's K/V, pa_prefill_chunk for the
-requests given more than one token, and pa_decode for the ones given exactly
-one. Marshalling and sequencing only; the work runs in libpa.so's kernels.
+the GPU, pa_write_kv for the K/V of the requests given more than one token,
+pa_prefill_chunk for those requests, and pa_decode_append for the ones given
+exactly one (their new K/V is stored by the decode itself). Marshalling and
+sequencing only; the work runs in libpa.so's kernels.
 """
 from __future__ import annotations
 
@@ -113,14 +114,16 @@ class StepRunner:
         seq = self.meta[o_seq:o_tab]
         tables = self.meta[o_tab:o_slot].view(S, mb)
         slots = self.meta[o_slot:end]
-        pa.pa_write_kv(self.desc, key[:N], value[:N], self.k, self.v, slots)
         n_pf = int(batch.query_start_loc[-1])
         if P:
+            pa.pa_write_kv(self.desc, key[:n_pf], value[:n_pf], self.k, self.v, slots[:n_pf])
             pa.pa_prefill_chunk(self.desc, out[:n_pf], q[:n_pf], self.k, self.v, qsl, seq[:P], tables[:P],
                                 int(batch.counts[:P].max()), int(batch.seq_lens[:P].max()), self.scale)
         if S > P:
             need = pa.pa_decode_workspace_size(self.desc, S - P, int(batch.seq_lens[P:].max()))
             if need > self.ws_bytes:
                 raise ValueError("decode workspace too small for this step")
-            pa.pa_decode(self.desc, out[n_pf:N], q[n_pf:N], self.k, self.v, tables[P:], seq[P:],
-                         int(batch.seq_lens[P:].max()), self.scale, self.ws)
+            # a one-token request's new token is its newest, at position seq_len - 1
+            pa.pa_decode_append(self.desc, out[n_pf:N], q[n_pf:N], key[n_pf:N], value[n_pf:N], self.k,
+                                self.v, tables[P:], seq[P:], int(batch.seq_lens[P:].max()), self.scale,
+                                self.ws)
