@@ -460,6 +460,26 @@ __global__ __launch_bounds__(64) void decode_merge_balanced_kernel(DecodeArgs a)
     for (int e = 0; e < kE; ++e) O[orow + e] = 0x7fc0;
     return;
   }
+  // append mode: the newest token's q, K, V and block id are loaded first, so
+  // that they share round trips with the loads that find and read the partials
+  const int kvh = h / a.group;
+  const int last = L - 1;
+  float qf[kE];
+  uint32_t kb[kE], vb[kE];
+  int32_t id = 0;
+  if constexpr (kAppend) {
+    const int64_t nrow = ((int64_t)s * a.num_kv_heads + kvh) * D + kE * lane;
+    const uint16_t* qp = (const uint16_t*)a.q + orow;
+    const uint16_t* kp = (const uint16_t*)a.new_k + nrow;
+    const uint16_t* vp = (const uint16_t*)a.new_v + nrow;
+#pragma unroll
+    for (int e = 0; e < kE; ++e) {
+      qf[e] = bf16_bits_to_f32(qp[e]);
+      kb[e] = kp[e];
+      vb[e] = vp[e];
+    }
+    id = a.block_tables[(int64_t)s * a.max_blocks + (last >> 4)];
+  }
   const int64_t T = a.cum_blocks[a.num_seqs];
   const int64_t c0 = a.cum_blocks[s], c1 = a.cum_blocks[s + 1];
   int np = 0;
@@ -476,19 +496,9 @@ __global__ __launch_bounds__(64) void decode_merge_balanced_kernel(DecodeArgs a)
   float o[kE], den, M;
   fold_partials<D>(a, row0, a.num_q_heads, np, lane, o, den, M);
   if constexpr (kAppend) {
-    const int kvh = h / a.group;
-    const int64_t nrow = ((int64_t)s * a.num_kv_heads + kvh) * D + kE * lane;
-    const uint16_t* qp = (const uint16_t*)a.q + orow;
-    const uint16_t* kp = (const uint16_t*)a.new_k + nrow;
-    const uint16_t* vp = (const uint16_t*)a.new_v + nrow;
-    uint32_t kb[kE], vb[kE];
     float part = 0.f;
 #pragma unroll
-    for (int e = 0; e < kE; ++e) {
-      kb[e] = kp[e];
-      vb[e] = vp[e];
-      part = __builtin_fmaf(bf16_bits_to_f32(qp[e]), bf16_bits_to_f32(kb[e]), part);
-    }
+    for (int e = 0; e < kE; ++e) part = __builtin_fmaf(qf[e], bf16_bits_to_f32(kb[e]), part);
     const float sn = wave_sum(part) * a.scale_log2;  // the same value in every lane
     const float mb = fmaxf(M, sn);
     const float alpha = fast_exp2(M - mb);  // 0 when there is no partial
@@ -496,8 +506,6 @@ __global__ __launch_bounds__(64) void decode_merge_balanced_kernel(DecodeArgs a)
     den = den * alpha + wn;
 #pragma unroll
     for (int e = 0; e < kE; ++e) o[e] = __builtin_fmaf(wn, bf16_bits_to_f32(vb[e]), o[e] * alpha);
-    const int last = L - 1;
-    const int32_t id = a.block_tables[(int64_t)s * a.max_blocks + (last >> 4)];
     if (!block_ok(id, a.num_blocks)) {
       den = __builtin_nanf("");  // as for any out-of-range block id
     } else if (h % a.group == 0) {

@@ -202,3 +202,42 @@ def test_append_block_boundaries(workers, monkeypatch):
     out = check_append(w, 0, f"append workers {workers}")
     # a context of one token returns that token's V exactly
     assert np.array_equal(host_bits(out)[0], np.repeat(w.step_write.value[0], 4, axis=0))
+
+
+@pytest.mark.parametrize("dtype,group,D", [("bf16", g, D) for g in (1, 2, 4, 8, 16) for D in (64, 128)]
+                         + [("f32", g, D) for g in (1, 4) for D in (64, 128)])
+def test_append_shapes(dtype, group, D):
+    """Every GQA group and head dim, balanced split (bf16: newest token attended by the merge;
+    f32: stored first) and fixed partitions (stored first)."""
+    w = workloads.custom_decode(300 + group + D, [1, 15, 16, 17, 31, 33, 300, 1111], Hq=2 * group,
+                                Hkv=2, D=D, dtype=dtype)
+    check_append(w, 0, f"append {dtype} G={group} D={D}")
+    check_append(w, 64, f"append {dtype} G={group} D={D} split 64")
+
+
+@pytest.mark.parametrize("part", [0, 64])
+def test_append_bad_length_and_block(part):
+    """A zero length, and an out-of-range id for the block of the newest token: that request's
+    output is NaN and nothing is stored for it; the other requests are unaffected."""
+    say(f"  decode_append bad inputs, partition {part}")
+    w = workloads.custom_decode(13, [5, 40, 17, 33], Hq=4, Hkv=2, D=64, dtype="bf16")
+    d, k, v = gpu_pools(w, include_step=False)
+    dec, sw = w.decode, w.step_write
+    lens = dec.context_lens.copy()
+    lens[1] = 0
+    tables = dec.block_tables.copy()
+    tables[3, 2] = w.spec.num_blocks + 7  # positions 32..47: only request 3's newest token
+    q = device_tensor(dec.q, "bf16")
+    out = torch.zeros_like(q)
+    ws = pa.decode_workspace(d, 4, dec.max_context_len, part)
+    pa.pa_decode_append(d, out, q, device_tensor(sw.key, "bf16"), device_tensor(sw.value, "bf16"), k, v,
+                        i32(tables), i32(lens), dec.max_context_len, w.scale, ws, part)
+    torch.cuda.synchronize()
+    o = as64(out)
+    assert np.all(np.isnan(o[[1, 3]])), "bad requests must give NaN"
+    ok, ov = oracle_pools(w, include_step=False)
+    good = [0, 2]
+    oracle.write_kv(ok, ov, sw.key[good], sw.value[good], sw.slot_mapping[good])
+    assert np.array_equal(host_bits(k), ok) and np.array_equal(host_bits(v), ov)
+    ref = oracle_decode(w, ok, ov)
+    assert_close(o[good], ref[good], "bf16", "append, requests next to bad ones")
