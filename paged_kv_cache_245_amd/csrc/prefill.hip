@@ -15,8 +15,11 @@
 // 64 (four 16-token blocks), staged in double-buffered LDS, K and V both
 // row-major [64 keys][D] with their 16-byte chunks XOR-swizzled by row (no bank
 // conflicts for either operand read). Wavefronts 0-3 stage K and 4-7 stage V,
-// one block each, through registers: the next-but-one tile is loaded while the
-// current one is used and stored at its end (one barrier per tile).
+// one block each, with direct global-to-LDS loads (global_load_lds_dwordx4: each
+// instruction fills 1 KiB of LDS, lane l's 16 bytes at offset 16 l, so the
+// swizzle is applied on the source side). Tile t + 2 is loaded into the stage
+// tile t has just released, right after the barrier that ends tile t, and lands
+// while tile t + 1 is computed (one barrier per tile).
 // Per wavefront (32 rows) and tile, with MFMA 32x32x16 bf16:
 //   S^T[32 keys x 32 rows] = K . Q^T for each 32-key half (D/16 MFMAs each;
 //     Q^T stays in registers; K operands are read four chunks ahead). Lane
@@ -30,8 +33,10 @@
 // accumulation; the running max moves only when a tile exceeds it by 2^8, so the
 // output is rescaled rarely (exact: numerator and denominator share the max).
 // Only tiles that cross the causal diagonal evaluate the mask.
-// Masked scores are set to -inf by selection; keys beyond the context are
-// staged as zeros, so no NaN from unused slots can reach the products.
+// Masked scores are set to -inf by selection. Rows past the context are not
+// loaded: the stage keeps the finite rows of two tiles before (or the zeros it
+// starts with), so no NaN from unused pool slots can reach the products, and
+// their probabilities are exactly zero.
 // The tile loop is unrolled by two, so the LDS stage of every operand read is an
 // immediate offset.
 // Work items (request, kv head, query tile) run heaviest first: workgroup i of
@@ -53,6 +58,14 @@ constexpr int kThreads = 64 * kWaves;
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+// Transposed 8-byte LDS read. Reached through a restrict pointer, the read
+// carries an alias scope, so the compiler does not hold it behind the
+// direct-to-LDS loads of the other stage still in flight (the kernel orders
+// those itself: a wait and a barrier before any stage is read).
+__device__ __forceinline__ v4i16 lds_read_tr(const lds_v4i16* __restrict__ p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p);
+}
 
 // Physical 16-byte chunk of logical chunk `ch` in row `row` of a staged tile.
 // K rows: the row's low 4 bits (16-lane K reads hit 16 distinct chunks).
@@ -240,8 +253,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
   // Staging: wavefronts 0-3 copy K, 4-7 copy V; wavefront w takes block w % 4 of
   // the tile. Piece i of lane l is LDS chunk slot ((w%4)*kInstr + i)*64 + l, i.e.
   // row slot/kCh, physical chunk slot%kCh, which holds logical chunk
-  // k_phys/v_phys(row, physical). Pieces go to registers at the top of a tile and
-  // are stored to the other LDS stage at its end.
+  // k_phys/v_phys(row, physical): each piece is one direct global-to-LDS load.
   const int sblk = wave & 3;          // block of the tile this wavefront copies
   const bool s_is_v = wave >= 4;      // wavefront-uniform
   int src_off[kInstr];                // element offsets inside a block (tile-independent)
@@ -252,7 +264,6 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
     const int ch = s_is_v ? v_phys<kCh>(row, slot % kCh) : k_phys<kCh>(row, slot % kCh);
     src_off[i] = (row & 15) * row_elems + kvh * D + 8 * ch;
   }
-  u32x4 sreg[kInstr];
   // block ids this wavefront copies, 64 tiles at a time: lane j holds tile id_tile0 + j
   int id_tile0 = 0;
   auto fetch_ids = [&]() {
@@ -260,7 +271,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
     return blk < nblocks ? table[blk] : 0;
   };
   int32_t idv = fetch_ids();
-  auto stage_load = [&](int t) {
+  typedef __attribute__((address_space(3))) void lds_void;
+  auto stage_load = [&](int t, int buf) {
     const int key0 = t * kBN;
     if (t - id_tile0 >= 64) {  // tiles are staged in order
       id_tile0 += 64;
@@ -269,18 +281,15 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
     int32_t id = __builtin_amdgcn_readlane(idv, t - id_tile0);
     if (!block_ok(id, a.num_blocks)) { poisoned = true; id = 0; }
     const uint16_t* src = (s_is_v ? a.v : a.k) + (int64_t)id * block_elems;
+    u32x4* dst = s_is_v ? &Vs[buf][0] : &Ks[buf][0];
     const bool full = key0 + 16 * (sblk + 1) <= L;  // uniform: the whole block is in range
 #pragma unroll
     for (int i = 0; i < kInstr; ++i) {
       const int row = ((sblk * kInstr + i) * 64 + lane) / kCh;
-      const bool in = full || key0 + row < L;  // past the context: zeros
-      sreg[i] = in ? *(const u32x4*)(src + src_off[i]) : u32x4{0, 0, 0, 0};
+      if (full || key0 + row < L)  // past the context: not loaded
+        __builtin_amdgcn_global_load_lds((const void*)(src + src_off[i]),
+                                         (lds_void*)&dst[(sblk * kInstr + i) * 64], 16, 0, 0);
     }
-  };
-  auto stage_store = [&](int buf) {
-    u32x4* dst = s_is_v ? &Vs[buf][0] : &Ks[buf][0];
-#pragma unroll
-    for (int i = 0; i < kInstr; ++i) dst[(sblk * kInstr + i) * 64 + lane] = sreg[i];
   };
 
   // Per-lane LDS byte addresses of the MFMA operands in stage 0 (stage 1 is +kTileCh*16).
@@ -309,10 +318,18 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
   float m = -INFINITY;  // running max (log2 units), moved only when exceeded by kRescale
   float lsum = 0.f;
 
-  stage_load(0);
-  stage_store(0);
+  // the stages start as zeros (rows past the context are never loaded)
+  for (int i = tid; i < 2 * kTileCh; i += kThreads) {
+    (&Ks[0][0])[i] = u32x4{0, 0, 0, 0};
+    (&Vs[0][0])[i] = u32x4{0, 0, 0, 0};
+  }
   __syncthreads();
-  if (n_tiles > 1) stage_load(1);
+  stage_load(0, 0);
+  if (n_tiles > 1) stage_load(1, 1);
+  // both tiles landed (a partial count would not do: rows past the context skip
+  // their loads) and are visible to every wavefront
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
 
   // one tile; the LDS stage is a compile-time constant so that operand
   // addresses take it as an immediate offset
@@ -405,8 +422,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
       v4i16 vlo[kAhead], vhi[kAhead];
       auto vread = [&](int j, int r) {
         const uint32_t base = v_addr[j % (D / 32)] + voff + (j / (D / 32)) * 16 * kCh * 16;
-        vlo[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(uintptr_t)base);
-        vhi[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(uintptr_t)(base + 8 * kCh * 16));
+        vlo[r] = lds_read_tr((const lds_v4i16*)(uintptr_t)base);
+        vhi[r] = lds_read_tr((const lds_v4i16*)(uintptr_t)(base + 8 * kCh * 16));
       };
 #pragma unroll
       for (int j = 0; j < kAhead; ++j) vread(j, j);
@@ -421,10 +438,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    // tile t+1 goes to the other stage, last read by tile t-1 (before the last barrier)
-    if (t + 1 < n_tiles) stage_store(buf ^ 1);
+    // tile t+1 (this wavefront's loads, issued a tile ago) has landed; after the
+    // barrier every wavefront's has, and tile t's stage is free for tile t+2
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (t + 2 < n_tiles) stage_load(t + 2);
+    if (t + 2 < n_tiles) stage_load(t + 2, buf);
   };
   for (int t = 0; t < n_tiles; t += 2) {
     tile_step(t, std::integral_constant<int, 0>{});
