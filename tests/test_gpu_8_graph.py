@@ -1,0 +1,93 @@
+"""A whole continuous-batching step captured once in a HIP graph and replayed.
+
+The step is pa_write_kv of the prefill rows, pa_prefill_chunk, and
+pa_decode_append for the one-token requests. No call of the step allocates,
+clears memory or synchronizes (outside PA_CHECK mode), so the step can be
+captured. Each replay runs with new q/K/V copied into the captured buffers,
+and its output and pools must equal, bit for bit, those of the same calls
+launched one by one on a second pair of pools. That eager step runs between
+the replays, with synchronizations in between.
+"""
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_245_amd as pa
+import workloads
+from gpu_support import device_tensor, gpu_pools, i32, say
+from workloads import f32_to_bf16_bits
+
+pytestmark = pytest.mark.gpu
+
+
+def bits(t):
+    return t.view(torch.int16).cpu().numpy()
+
+
+def test_step_graph_replays_match_eager():
+    say("  graph capture of a mixed step")
+    w = workloads.custom_prefill(21, cached=[0, 40, 100], new=[30, 17, 64], Hq=8, Hkv=2, D=128,
+                                 dtype="bf16", decode_lengths=[1, 16, 17, 200, 513])
+    d, k0, v0 = gpu_pools(w, include_step=False)
+    st, p, dec = w.step_write, w.prefill, w.decode
+    P, T = w.num_prefills, p.q.shape[0]
+    n_tok = st.key.shape[0]
+
+    q = device_tensor(w.query, "bf16")
+    key, value = device_tensor(st.key, "bf16"), device_tensor(st.value, "bf16")
+    slots = i32(st.slot_mapping[:T])
+    tables = i32(w.block_tables)
+    qsl, seq = i32(p.query_start_loc), i32(p.seq_lens)
+    lens = i32(dec.context_lens)
+    ws = pa.decode_workspace(d, len(dec.context_lens), dec.max_context_len)
+    scale = w.scale
+
+    def step(k, v, out):
+        pa.pa_write_kv(d, key[:T], value[:T], k, v, slots)
+        pa.pa_prefill_chunk(d, out[:T], q[:T], k, v, qsl, seq, tables[:P], p.max_query_len, p.max_seq_len,
+                            scale)
+        pa.pa_decode_append(d, out[T:], q[T:], key[T:], value[T:], k, v, tables[P:], lens,
+                            dec.max_context_len, scale, ws)
+
+    kg, vg = k0.clone(), v0.clone()
+    out_g = torch.empty_like(q)
+    ke, ve = k0.clone(), v0.clone()
+    out_e = torch.empty_like(q)
+
+    # one eager run on the side stream before capture, as torch asks
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(ke, ve, out_e)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(kg, vg, out_g)
+    torch.cuda.synchronize()
+
+    rng = np.random.default_rng(5)
+    outs = []
+    for rep in range(3):
+        # new inputs into the captured buffers, both pool pairs back to the set-up state
+        q.copy_(torch.from_numpy(f32_to_bf16_bits(rng.standard_normal(tuple(q.shape), dtype=np.float32))
+                                 .view(np.int16)).view(torch.bfloat16).cuda())
+        for t in (key, value):
+            t.copy_(torch.from_numpy(f32_to_bf16_bits(rng.standard_normal((n_tok,) + tuple(t.shape[1:]),
+                                                                          dtype=np.float32))
+                                     .view(np.int16)).view(torch.bfloat16).cuda())
+        for dst, src in ((kg, k0), (vg, v0), (ke, k0), (ve, v0)):
+            dst.copy_(src)
+        out_g.zero_()
+        out_e.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        step(ke, ve, out_e)  # eager work between the replays
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(out_g), bits(out_e)), f"replay {rep}: output"
+        assert np.array_equal(bits(kg), bits(ke)) and np.array_equal(bits(vg), bits(ve)), f"replay {rep}: pools"
+        assert np.all(np.isfinite(out_g.float().cpu().numpy()))
+        outs.append(bits(out_g))
+    assert not np.array_equal(outs[0], outs[1])  # the replays did see the new inputs
