@@ -454,16 +454,16 @@ __global__ __launch_bounds__(64) void decode_merge_balanced_kernel(DecodeArgs a)
   const int s = blockIdx.y;
   uint16_t* O = (uint16_t*)a.out;
   const int64_t orow = ((int64_t)s * a.num_q_heads + h) * D + kE * lane;
+  // The kernel is a short chain of dependent loads, so it is written without
+  // early branches: the request's length, the block prefix sums that locate its
+  // partials and, in append mode, the newest token's q, K, V and block id are
+  // all requested first (every index is in range whatever their values); the
+  // partials follow.
   const int L = min(a.context_lens[s], a.max_context_len);
-  if (L <= 0) {
-#pragma unroll
-    for (int e = 0; e < kE; ++e) O[orow + e] = 0x7fc0;
-    return;
-  }
-  // append mode: the newest token's q, K, V and block id are loaded first, so
-  // that they share round trips with the loads that find and read the partials
+  const int64_t T = a.cum_blocks[a.num_seqs];
+  const int64_t c0 = a.cum_blocks[s], c1 = a.cum_blocks[s + 1];
   const int kvh = h / a.group;
-  const int last = L - 1;
+  const int last = max(L - 1, 0);
   float qf[kE];
   uint32_t kb[kE], vb[kE];
   int32_t id = 0;
@@ -478,21 +478,17 @@ __global__ __launch_bounds__(64) void decode_merge_balanced_kernel(DecodeArgs a)
       kb[e] = kp[e];
       vb[e] = vp[e];
     }
-    id = a.block_tables[(int64_t)s * a.max_blocks + (last >> 4)];
+    id = a.block_tables[(int64_t)s * a.max_blocks + (last >> 4)];  // last < 16 * max_blocks
   }
-  const int64_t T = a.cum_blocks[a.num_seqs];
-  const int64_t c0 = a.cum_blocks[s], c1 = a.cum_blocks[s + 1];
-  int np = 0;
-  int64_t row0 = 0;
-  if (c1 > c0) {
-    const int W = (int)min((int64_t)a.num_workers, T);  // as in the decode kernel
-    const int w0 = worker_of(c0, T, W);
-    const int w1 = worker_of(c1 - 1, T, W);
-    if (!kAppend && w0 == w1) return;  // one segment: written by the decode kernel
-    np = w1 - w0 + 1;
-    // partial of worker w0 + i for this (request, head) is row (s + w0 + i) * Hq + h
-    row0 = ((int64_t)s + w0) * a.num_q_heads + h;
-  }
+  const int64_t Tn = max(T, (int64_t)1);
+  const int W = (int)min((int64_t)a.num_workers, Tn);  // as in the decode kernel
+  const int w0 = worker_of(c0, Tn, W);
+  const int w1 = worker_of(max(c1 - 1, c0), Tn, W);
+  const bool has_blocks = c1 > c0;  // false for L <= 0
+  if (!kAppend && L > 0 && w0 == w1) return;  // one segment: written by the decode kernel
+  const int np = has_blocks ? w1 - w0 + 1 : 0;
+  // partial of worker w0 + i for this (request, head) is row (s + w0 + i) * Hq + h
+  const int64_t row0 = ((int64_t)s + w0) * a.num_q_heads + h;
   float o[kE], den, M;
   fold_partials<D>(a, row0, a.num_q_heads, np, lane, o, den, M);
   if constexpr (kAppend) {
@@ -508,7 +504,7 @@ __global__ __launch_bounds__(64) void decode_merge_balanced_kernel(DecodeArgs a)
     for (int e = 0; e < kE; ++e) o[e] = __builtin_fmaf(wn, bf16_bits_to_f32(vb[e]), o[e] * alpha);
     if (!block_ok(id, a.num_blocks)) {
       den = __builtin_nanf("");  // as for any out-of-range block id
-    } else if (h % a.group == 0) {
+    } else if (L > 0 && h % a.group == 0) {
       const int64_t row = kv_row(id, last & 15, kvh, a.num_kv_heads, D) + kE * lane;
 #pragma unroll
       for (int e = 0; e < kE; ++e) {
@@ -517,6 +513,7 @@ __global__ __launch_bounds__(64) void decode_merge_balanced_kernel(DecodeArgs a)
       }
     }
   }
+  if (L <= 0) den = __builtin_nanf("");  // no key (in append mode, no newest token): NaN
   const float inv = 1.f / den;
   if constexpr (kE == 2)
     *(uint32_t*)(O + orow) = pack_bf16x2(o[0] * inv, o[1] * inv);
