@@ -1,0 +1,85 @@
+"""Slots outside a request's logical context never reach its output.
+
+Paged attention computes attention over each request's logical context only
+(intro to vLLM's paged attention, section "PagedAttention"). Slots outside
+that context are: the tail of a request's last block, spare blocks, and the
+spare block that pads every block table. Each path runs twice on the same
+keys, once over pools filled with quiet NaN and once over pools filled with
+zeros. The outputs must be finite and equal bit for bit. A kernel that
+multiplied an unused slot by a zero weight, instead of selecting it out,
+would turn NaN into the output.
+"""
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_245_amd as pa
+import workloads
+from gpu_support import desc_of, device_tensor, gpu_pools, host_bits, i32, run_decode, run_prefill, say, write
+
+pytestmark = pytest.mark.gpu
+
+
+def zero_pools(w, include_step=True):
+    d = desc_of(w)
+    dt = torch.bfloat16 if w.spec.dtype == "bf16" else torch.float32
+    k = torch.zeros(w.spec.pool_shape(), dtype=dt, device="cuda")
+    v = torch.zeros_like(k)
+    write(w, d, k, v, w.setup)
+    if include_step:
+        write(w, d, k, v, w.step_write)
+    return d, k, v
+
+
+def same_bits(a, b, what):
+    x, y = host_bits(a), host_bits(b)
+    if x.dtype == np.float32:
+        x, y = x.view(np.uint32), y.view(np.uint32)
+    assert np.array_equal(x, y), f"{what}: output depends on slots outside the context"
+    f = a.float().cpu().numpy()
+    assert np.all(np.isfinite(f)), f"{what}: non-finite output"
+
+
+def decode_lengths():
+    # every tail length of a last block, and lengths that end on a block boundary
+    return [1, 2, 15, 16, 17, 31, 33, 47, 64, 95, 130, 257, 700, 1023]
+
+
+@pytest.mark.parametrize("dtype,part", [("bf16", 0), ("bf16", 64), ("bf16", 512), ("f32", 0)])
+def test_decode(dtype, part):
+    say(f"  poison vs zeros: decode {dtype} partition {part}")
+    w = workloads.custom_decode(91, decode_lengths(), Hq=8, Hkv=2, D=128, dtype=dtype)
+    assert (w.decode.block_tables >= 0).all(), "the pool has a spare block for table padding"
+    _, kp, vp = gpu_pools(w)
+    _, kz, vz = zero_pools(w)
+    same_bits(run_decode(w, desc_of(w), kp, vp, part), run_decode(w, desc_of(w), kz, vz, part), "decode")
+
+
+def run_append(w, d, k, v):
+    dec, sw = w.decode, w.step_write
+    q = device_tensor(dec.q, w.spec.dtype)
+    out = torch.empty_like(q)
+    ws = pa.decode_workspace(d, len(dec.context_lens), dec.max_context_len)
+    pa.pa_decode_append(d, out, q, device_tensor(sw.key, w.spec.dtype), device_tensor(sw.value, w.spec.dtype),
+                        k, v, i32(dec.block_tables), i32(dec.context_lens), dec.max_context_len, w.scale, ws)
+    torch.cuda.synchronize()
+    return out
+
+
+def test_decode_append():
+    say("  poison vs zeros: decode_append")
+    w = workloads.custom_decode(92, decode_lengths(), Hq=8, Hkv=2, D=128, dtype="bf16")
+    d, kp, vp = gpu_pools(w, include_step=False)
+    _, kz, vz = zero_pools(w, include_step=False)
+    same_bits(run_append(w, d, kp, vp), run_append(w, d, kz, vz), "decode_append")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_prefill(D):
+    """Chunks whose contexts end inside a block, in the first tile and further on."""
+    say(f"  poison vs zeros: prefill D={D}")
+    w = workloads.custom_prefill(93 + D, cached=[0, 5, 63, 64, 100, 1000], new=[1, 16, 3, 70, 37, 200],
+                                 Hq=8, Hkv=2, D=D, dtype="bf16")
+    d, kp, vp = gpu_pools(w)
+    _, kz, vz = zero_pools(w)
+    same_bits(run_prefill(w, d, kp, vp), run_prefill(w, d, kz, vz), "prefill")
