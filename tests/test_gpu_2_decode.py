@@ -241,3 +241,14 @@ def test_append_bad_length_and_block(part):
     assert np.array_equal(host_bits(k), ok) and np.array_equal(host_bits(v), ov)
     ref = oracle_decode(w, ok, ov)
     assert_close(o[good], ref[good], "bf16", "append, requests next to bad ones")
+
+
+@pytest.mark.parametrize("S", [8192, 8193])
+def test_batch_size_limit(S):
+    """The largest batch the balanced split takes (its block prefix sums fill LDS) and one more
+    request, which goes to fixed partitions; plain decode and decode-append alike."""
+    say(f"  decode batch of {S} requests")
+    lens = np.random.default_rng(S).integers(1, 81, S).tolist()
+    w = workloads.custom_decode(S, lens, Hq=8, Hkv=2, D=64, dtype="bf16")
+    check(w, 0, f"{S} requests")
+    check_append(w, 0, f"append, {S} requests")
