@@ -116,6 +116,34 @@ def _need(t, dtype, name, ndim=None):
         raise ValueError(f"{name} must have {ndim} dimensions")
 
 
+def _shape(t, name, *dims):
+    """The kernels trust the sizes they are given: t must be exactly [dims] (None: any size)."""
+    if t.dim() != len(dims) or any(d is not None and t.shape[i] != d for i, d in enumerate(dims)):
+        want = ", ".join("*" if d is None else str(d) for d in dims)
+        raise ValueError(f"{name} must be [{want}], got {list(t.shape)}")
+
+
+def _pools(desc, k_cache, v_cache):
+    for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        _shape(t, n, desc.num_blocks, BLOCK_SIZE, desc.num_kv_heads, desc.head_dim)
+
+
+def _rows(t, name, n, *tail):
+    """t is [m, *tail] with m >= n rows (rows past n are neither read nor written)."""
+    if t.dim() != 1 + len(tail) or t.shape[0] < n or tuple(t.shape[1:]) != tuple(tail):
+        want = ", ".join(str(x) for x in tail)
+        raise ValueError(f"{name} must be [>= {n}, {want}], got {list(t.shape)}")
+
+
+def _table_rows(block_tables, S):
+    if block_tables.shape[0] < S:
+        raise ValueError(f"block_tables has {block_tables.shape[0]} rows for {S} requests")
+
+
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
 def pa_version() -> int:
     return load().pa_version()
 
@@ -135,8 +163,9 @@ def pa_write_kv(desc, key, value, k_cache, v_cache, slot_mapping, stream=None):
         _need(t, dt, n)
     _need(slot_mapping, torch.int32, "slot_mapping", 1)
     n = slot_mapping.numel()
-    if key.shape[0] != n or value.shape[0] != n:
-        raise ValueError("key/value rows must match slot_mapping")
+    _pools(desc, k_cache, v_cache)
+    _rows(key, "key", n, desc.num_kv_heads, desc.head_dim)
+    _rows(value, "value", n, desc.num_kv_heads, desc.head_dim)
     st = load().pa_write_kv(ctypes.byref(desc), _ptr(key), _ptr(value), _ptr(k_cache),
                             _ptr(v_cache), _ptr(slot_mapping), n, _stream(stream, k_cache))
     _check(st, "pa_write_kv")
@@ -168,7 +197,11 @@ def pa_decode(desc, out, q, k_cache, v_cache, block_tables, context_lens, max_co
     _need(block_tables, torch.int32, "block_tables", 2)
     _need(context_lens, torch.int32, "context_lens", 1)
     S = context_lens.numel()
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _pools(desc, k_cache, v_cache)
+    _rows(q, "q", S, desc.num_q_heads, desc.head_dim)
+    _rows(out, "out", S, desc.num_q_heads, desc.head_dim)
+    _table_rows(block_tables, S)
+    ws_bytes = _nbytes(workspace) if workspace is not None else 0
     st = load().pa_decode(ctypes.byref(desc), _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
                           _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), S,
                           int(max_context_len), float(scale), int(partition_tokens),
@@ -187,9 +220,13 @@ def pa_decode_append(desc, out, q, key, value, k_cache, v_cache, block_tables, c
     _need(block_tables, torch.int32, "block_tables", 2)
     _need(context_lens, torch.int32, "context_lens", 1)
     S = context_lens.numel()
-    if key.shape[0] != S or value.shape[0] != S:
-        raise ValueError("key/value need one row per request")
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _pools(desc, k_cache, v_cache)
+    _rows(q, "q", S, desc.num_q_heads, desc.head_dim)
+    _rows(out, "out", S, desc.num_q_heads, desc.head_dim)
+    _rows(key, "key", S, desc.num_kv_heads, desc.head_dim)
+    _rows(value, "value", S, desc.num_kv_heads, desc.head_dim)
+    _table_rows(block_tables, S)
+    ws_bytes = _nbytes(workspace) if workspace is not None else 0
     st = load().pa_decode_append(ctypes.byref(desc), _ptr(out), _ptr(q), _ptr(key), _ptr(value),
                                  _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), block_tables.shape[1],
                                  _ptr(context_lens), S, int(max_context_len), float(scale),
@@ -207,6 +244,11 @@ def pa_prefill_chunk(desc, out, q, k_cache, v_cache, query_start_loc, seq_lens, 
         _need(t, torch.int32, n, 1)
     _need(block_tables, torch.int32, "block_tables", 2)
     S = seq_lens.numel()
+    _pools(desc, k_cache, v_cache)
+    _rows(q, "q", 0, desc.num_q_heads, desc.head_dim)
+    _rows(out, "out", q.shape[0], desc.num_q_heads, desc.head_dim)
+    _shape(query_start_loc, "query_start_loc", S + 1)
+    _table_rows(block_tables, S)
     st = load().pa_prefill_chunk(ctypes.byref(desc), _ptr(out), _ptr(q), _ptr(k_cache),
                                  _ptr(v_cache), _ptr(query_start_loc), _ptr(seq_lens),
                                  _ptr(block_tables), block_tables.shape[1], S, q.shape[0],
@@ -221,8 +263,8 @@ def pa_copy_blocks(desc, k_cache, v_cache, block_pairs, stream=None):
     _need(k_cache, dt, "k_cache")
     _need(v_cache, dt, "v_cache")
     _need(block_pairs, torch.int32, "block_pairs", 2)
-    if block_pairs.shape[1] != 2:
-        raise ValueError("block_pairs must be [n, 2]")
+    _pools(desc, k_cache, v_cache)
+    _shape(block_pairs, "block_pairs", None, 2)
     st = load().pa_copy_blocks(ctypes.byref(desc), _ptr(k_cache), _ptr(v_cache), _ptr(block_pairs),
                                block_pairs.shape[0], _stream(stream, k_cache))
     _check(st, "pa_copy_blocks")
@@ -242,9 +284,10 @@ def pa_swap_blocks(desc, k_cache, v_cache, host_k, host_v, block_pairs, directio
         raise ValueError("host_k/host_v must be pinned CPU tensors")
     if host_k.shape != host_v.shape or not host_k.is_contiguous() or not host_v.is_contiguous():
         raise ValueError("host_k/host_v must be contiguous and of one shape")
+    _pools(desc, k_cache, v_cache)
+    _shape(host_k, "host_k", None, BLOCK_SIZE, desc.num_kv_heads, desc.head_dim)
     _need(block_pairs, torch.int32, "block_pairs", 2)
-    if block_pairs.shape[1] != 2:
-        raise ValueError("block_pairs must be [n, 2]")
+    _shape(block_pairs, "block_pairs", None, 2)
     st = load().pa_swap_blocks(ctypes.byref(desc), _ptr(k_cache), _ptr(v_cache),
                                ctypes.c_void_p(host_k.data_ptr()), ctypes.c_void_p(host_v.data_ptr()),
                                host_k.shape[0], _ptr(block_pairs), block_pairs.shape[0], int(direction),
@@ -255,8 +298,16 @@ def pa_swap_blocks(desc, k_cache, v_cache, host_k, host_v, block_pairs, directio
 def pa_gather_kv(desc, dst_k, dst_v, k_cache, v_cache, block_tables, context_lens,
                  max_context_len, stream=None):
     """dst_k/dst_v [S, max_context_len, Hkv, D]: each request's logical K/V rows."""
+    dt = torch_dtype(desc)
+    for t, n in ((dst_k, "dst_k"), (dst_v, "dst_v"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _need(t, dt, n)
     _need(block_tables, torch.int32, "block_tables", 2)
     _need(context_lens, torch.int32, "context_lens", 1)
+    S = context_lens.numel()
+    _pools(desc, k_cache, v_cache)
+    for t, n in ((dst_k, "dst_k"), (dst_v, "dst_v")):
+        _shape(t, n, S, int(max_context_len), desc.num_kv_heads, desc.head_dim)
+    _table_rows(block_tables, S)
     st = load().pa_gather_kv(ctypes.byref(desc), _ptr(dst_k), _ptr(dst_v), _ptr(k_cache),
                              _ptr(v_cache), _ptr(block_tables), block_tables.shape[1],
                              _ptr(context_lens), context_lens.numel(), int(max_context_len),
@@ -265,12 +316,18 @@ def pa_gather_kv(desc, dst_k, dst_v, k_cache, v_cache, block_tables, context_len
 
 
 def pa_bench_copy(dst, src, nbytes, stream=None):
+    if nbytes > min(_nbytes(dst), _nbytes(src)):
+        raise ValueError("nbytes exceeds a buffer")
     _check(load().pa_bench_copy(_ptr(dst), _ptr(src), nbytes, _stream(stream, src)), "pa_bench_copy")
 
 
 def pa_bench_read(src, nbytes, sink, stream=None):
+    if nbytes > _nbytes(src) or _nbytes(sink) < 4096 * 4:
+        raise ValueError("nbytes exceeds src, or sink holds fewer than 4096 floats")
     _check(load().pa_bench_read(_ptr(src), nbytes, _ptr(sink), _stream(stream, src)), "pa_bench_read")
 
 
 def pa_bench_flush(buf, nbytes, stream=None):
+    if nbytes > _nbytes(buf):
+        raise ValueError("nbytes exceeds buf")
     _check(load().pa_bench_flush(_ptr(buf), nbytes, _stream(stream, buf)), "pa_bench_flush")

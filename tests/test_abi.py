@@ -171,10 +171,44 @@ def test_bench_argument_checks(lib):
 
 def test_binding_refuses_host_tensors(lib):
     import torch
-    d = desc(dtype="f32", num_q_heads=8, num_kv_heads=8, head_dim=64)
+    d = desc(dtype="f32", num_q_heads=8, num_kv_heads=8, head_dim=64, num_blocks=2)
     x = torch.zeros(4, 8, 64)
-    with pytest.raises(ValueError):
-        pa.pa_write_kv(d, x, x, x, x, torch.zeros(4, dtype=torch.int32))
+    pool = torch.zeros(2, 16, 8, 64)
+    with pytest.raises(ValueError, match="GPU"):
+        pa.pa_write_kv(d, x, x, pool, pool, torch.zeros(4, dtype=torch.int32))
+
+
+def test_binding_checks_shapes(lib):
+    """The C ABI takes plain pointers, so the binding refuses tensors whose shapes disagree
+    with the descriptor or with each other (checked before any pointer is taken)."""
+    import torch
+    bf = torch.bfloat16
+    d = desc(num_q_heads=8, num_kv_heads=2, head_dim=64, num_blocks=4)
+    pool, small = torch.zeros(4, 16, 2, 64, dtype=bf), torch.zeros(3, 16, 2, 64, dtype=bf)
+    kv, slots = torch.zeros(5, 2, 64, dtype=bf), torch.zeros(5, dtype=torch.int32)
+    with pytest.raises(ValueError, match="k_cache"):
+        pa.pa_write_kv(d, kv, kv, small, pool, slots)
+    with pytest.raises(ValueError, match="key"):
+        pa.pa_write_kv(d, kv[:4], kv, pool, pool, slots)  # fewer rows than slots
+    q = torch.zeros(3, 8, 64, dtype=bf)
+    tables, lens = torch.zeros(3, 4, dtype=torch.int32), torch.ones(3, dtype=torch.int32)
+    with pytest.raises(ValueError, match="q must be"):
+        pa.pa_decode(d, q, q[:2], pool, pool, tables, lens, 16, 0.1)
+    with pytest.raises(ValueError, match="out must be"):
+        pa.pa_decode(d, torch.zeros(3, 8, 32, dtype=bf), q, pool, pool, tables, lens, 16, 0.1)
+    with pytest.raises(ValueError, match="block_tables"):
+        pa.pa_decode(d, q, q, pool, pool, tables[:2], lens, 16, 0.1)
+    with pytest.raises(ValueError, match="value"):
+        pa.pa_decode_append(d, q, q, kv[:3], kv[:2], pool, pool, tables, lens, 16, 0.1)
+    with pytest.raises(ValueError, match="query_start_loc"):
+        pa.pa_prefill_chunk(d, q, q, pool, pool, torch.zeros(3, dtype=torch.int32), lens, tables, 1, 1, 0.1)
+    with pytest.raises(ValueError, match="block_pairs"):
+        pa.pa_copy_blocks(d, pool, pool, torch.zeros(2, 3, dtype=torch.int32))
+    with pytest.raises(ValueError, match="dst_k"):
+        pa.pa_gather_kv(d, torch.zeros(3, 8, 2, 64, dtype=bf), torch.zeros(3, 16, 2, 64, dtype=bf), pool, pool,
+                        tables, lens, 16)
+    with pytest.raises(ValueError, match="nbytes"):
+        pa.pa_bench_read(torch.zeros(16, dtype=torch.uint8), 32, torch.zeros(4096))
 
 
 def test_swap_and_copy_argument_checks(lib):
