@@ -161,9 +161,10 @@ int pa_prefill_chunk(const pa_cache_desc* desc, void* out, const void* q,
 /* Decode after appending each request's newest token: the same result as
  * pa_write_kv of those tokens into their slots followed by pa_decode. Where the
  * decode runs in its balanced bf16 mode (the default for bf16 pools,
- * partition_tokens == 0) no write launch is added: the decode reads the pool up
- * to each newest token, and its merge pass attends that token and stores it.
- * Otherwise the tokens are stored first, then the decode runs. The newest token of
+ * partition_tokens == 0) and the requests do not outnumber its workgroups (256
+ * with 8 kv heads), no write launch is added: the decode reads the pool up to
+ * each newest token, and its merge pass attends that token and stores it.
+ * Otherwise the tokens are stored first by a small kernel, then the decode runs. The newest token of
  * request s sits at position context_lens[s] - 1 (context_lens counts it); its
  * slot is read from the request's block table, so the block covering that
  * position must be in the table (and, when shared, already copied on write).

@@ -395,6 +395,11 @@ __device__ __forceinline__ int worker_of(int64_t b, int64_t T, int W) {
   return (int)(((b + 1) * W + T - 1) / T) - 1;
 }
 
+// q heads merged by one workgroup of decode_merge_balanced_kernel (one wavefront
+// each): with many short requests the merge is dispatch-bound, so workgroups
+// take several heads.
+constexpr int kMergeHeads = 8;
+
 // Merge of split-KV partials (m, l, acc) of one (request, q head): partial i is
 // row row0 + i * rstep of the workspace. Returns M = max_i m_i (-inf for none),
 // o = sum_i 2^(m_i - M) acc_i and den = sum_i 2^(m_i - M) l_i; the caller divides.
@@ -447,11 +452,12 @@ __device__ __forceinline__ void fold_partials(const DecodeArgs& a, int64_t row0,
 // into the request's slot at position L - 1, after the decode kernel has read
 // the pool.
 template <int D, bool kAppend>
-__global__ __launch_bounds__(64) void decode_merge_balanced_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64 * kMergeHeads) void decode_merge_balanced_kernel(DecodeArgs a) {
   constexpr int kE = D / 64;
-  const int lane = threadIdx.x;
-  const int h = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int h = blockIdx.x * kMergeHeads + (threadIdx.x >> 6);  // one wavefront per q head
   const int s = blockIdx.y;
+  if (h >= a.num_q_heads) return;  // whole wavefront; the kernel has no barrier
   uint16_t* O = (uint16_t*)a.out;
   const int64_t orow = ((int64_t)s * a.num_q_heads + h) * D + kE * lane;
   // The kernel is a short chain of dependent loads, so it is written without
@@ -519,6 +525,127 @@ __global__ __launch_bounds__(64) void decode_merge_balanced_kernel(DecodeArgs a)
     *(uint32_t*)(O + orow) = pack_bf16x2(o[0] * inv, o[1] * inv);
   else
     O[orow] = f32_to_bf16_bits(o[0] * inv);
+}
+
+// Balanced mode merge for requests split over many workers (many partials each):
+// 256 threads per (q head, request). Groups of D/4 threads own 4 dims each;
+// group g folds partials g, g + kG, g + 2 kG, ... (kG = 256 / (D/4) groups), so a
+// request split over hundreds of workers costs a few rounds of loads instead of
+// one round per eight partials. The group results are combined through LDS, and
+// group 0 finishes as decode_merge_balanced_kernel does (newest token included
+// in append mode).
+template <int D, bool kAppend>
+__global__ __launch_bounds__(256) void decode_merge_wide_kernel(DecodeArgs a) {
+  constexpr int kT = D / 4;     // threads per group, one float4 of dims each
+  constexpr int kG = 256 / kT;  // groups
+  constexpr int kBatch = 16;    // partials per group and round, all loads issued first
+  const int tid = threadIdx.x;
+  const int grp = tid / kT, ti = tid % kT;
+  const int h = blockIdx.x;
+  const int s = blockIdx.y;
+  uint16_t* O = (uint16_t*)a.out;
+  const int64_t orow = ((int64_t)s * a.num_q_heads + h) * D + 4 * ti;
+  // first round of loads, as in decode_merge_balanced_kernel
+  const int L = min(a.context_lens[s], a.max_context_len);
+  const int64_t T = a.cum_blocks[a.num_seqs];
+  const int64_t c0 = a.cum_blocks[s], c1 = a.cum_blocks[s + 1];
+  const int kvh = h / a.group;
+  const int last = max(L - 1, 0);
+  const int64_t Tn = max(T, (int64_t)1);
+  const int W = (int)min((int64_t)a.num_workers, Tn);  // as in the decode kernel
+  const int w0 = worker_of(c0, Tn, W);
+  const int w1 = worker_of(max(c1 - 1, c0), Tn, W);
+  if (!kAppend && L > 0 && w0 == w1) return;  // one segment: written by the decode kernel
+  const int np = c1 > c0 ? w1 - w0 + 1 : 0;
+  const int64_t row0 = ((int64_t)s + w0) * a.num_q_heads + h;
+  const int64_t rstep = a.num_q_heads;
+
+  float M = -INFINITY, den = 0.f;
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+  for (int i0 = grp; i0 < np; i0 += kG * kBatch) {
+    float mi[kBatch], li[kBatch];
+    f32x4 ai[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int i = i0 + j * kG;
+      const bool in = i < np;
+      const int64_t r = row0 + (int64_t)(in ? i : 0) * rstep;
+      mi[j] = in ? a.part_ml[2 * r] : -INFINITY;
+      li[j] = in ? a.part_ml[2 * r + 1] : 0.f;
+      ai[j] = in ? *(const f32x4*)(a.part_acc + r * D + 4 * ti) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    float mb = M;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) mb = fmaxf(mb, mi[j]);
+    const float alpha = fast_exp2(M - mb);  // the first partial of the group is real: mb is finite
+    den *= alpha;
+    o *= alpha;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const float wgt = fast_exp2(mi[j] - mb);  // 0 for padding
+      den += wgt * li[j];
+      o += wgt * ai[j];
+    }
+    M = mb;
+  }
+  __shared__ float sM[kG], sDen[kG];
+  __shared__ f32x4 sO[kG][kT];
+  if (ti == 0) {
+    sM[grp] = M;
+    sDen[grp] = den;
+  }
+  sO[grp][ti] = o;
+  __syncthreads();
+  if (grp != 0) return;  // no barrier below
+  float Mt = -INFINITY;
+#pragma unroll
+  for (int g = 0; g < kG; ++g) Mt = fmaxf(Mt, sM[g]);
+  den = 0.f;
+  o = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (Mt > -INFINITY) {  // else no partial at all
+#pragma unroll
+    for (int g = 0; g < kG; ++g) {
+      const float wgt = fast_exp2(sM[g] - Mt);  // 0 for groups without a partial
+      den += wgt * sDen[g];
+      o += wgt * sO[g][ti];
+    }
+  }
+  M = Mt;
+  if constexpr (kAppend) {
+    // the newest key as one more partial (m = its score, l = 1, acc = its V row)
+    const int64_t nrow = ((int64_t)s * a.num_kv_heads + kvh) * D + 4 * ti;
+    const u32x2 qw = *(const u32x2*)((const uint16_t*)a.q + orow);
+    const u32x2 kw = *(const u32x2*)((const uint16_t*)a.new_k + nrow);
+    const u32x2 vw = *(const u32x2*)((const uint16_t*)a.new_v + nrow);
+    const int32_t id = a.block_tables[(int64_t)s * a.max_blocks + (last >> 4)];
+    float part = 0.f;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      part = __builtin_fmaf(bf16_bits_to_f32(qw[e] & 0xffffu), bf16_bits_to_f32(kw[e] & 0xffffu), part);
+      part = __builtin_fmaf(bf16_bits_to_f32(qw[e] >> 16), bf16_bits_to_f32(kw[e] >> 16), part);
+    }
+#pragma unroll
+    for (int off = kT / 2; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);  // within the group
+    const float sn = part * a.scale_log2;
+    const float mb = fmaxf(M, sn);
+    const float alpha = fast_exp2(M - mb);  // 0 when there is no partial
+    const float wn = fast_exp2(sn - mb);
+    den = den * alpha + wn;
+    const float vv[4] = {bf16_bits_to_f32(vw[0] & 0xffffu), bf16_bits_to_f32(vw[0] >> 16),
+                         bf16_bits_to_f32(vw[1] & 0xffffu), bf16_bits_to_f32(vw[1] >> 16)};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = __builtin_fmaf(wn, vv[e], o[e] * alpha);
+    if (!block_ok(id, a.num_blocks)) {
+      den = __builtin_nanf("");  // as for any out-of-range block id
+    } else if (L > 0 && h % a.group == 0) {
+      const int64_t row = kv_row(id, last & 15, kvh, a.num_kv_heads, D) + 4 * ti;
+      *(u32x2*)((uint16_t*)a.k + row) = kw;
+      *(u32x2*)((uint16_t*)a.v + row) = vw;
+    }
+  }
+  if (L <= 0) den = __builtin_nanf("");  // no key (in append mode, no newest token): NaN
+  const float inv = 1.f / den;
+  *(u32x2*)(O + orow) = u32x2{pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv)};
 }
 
 // Fixed-partition mode: grid (partitions, kv-head groups, requests).
@@ -742,11 +869,18 @@ hipError_t launch_decode_d(const DecodeArgs& a, bool bf16, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 mgrid(a.num_q_heads, a.num_seqs);
+  dim3 hgrid((a.num_q_heads + kMergeHeads - 1) / kMergeHeads, a.num_seqs);
   if (a.num_workers > 0) {
-    if (a.new_k != nullptr)
-      hipLaunchKernelGGL((decode_merge_balanced_kernel<D, true>), mgrid, dim3(64), 0, stream, a);
+    // requests split over more than eight workers on average: the wide merge
+    const bool wide = a.num_workers > 8 * a.num_seqs;
+    if (wide && a.new_k != nullptr)
+      hipLaunchKernelGGL((decode_merge_wide_kernel<D, true>), mgrid, dim3(256), 0, stream, a);
+    else if (wide)
+      hipLaunchKernelGGL((decode_merge_wide_kernel<D, false>), mgrid, dim3(256), 0, stream, a);
+    else if (a.new_k != nullptr)
+      hipLaunchKernelGGL((decode_merge_balanced_kernel<D, true>), hgrid, dim3(64 * kMergeHeads), 0, stream, a);
     else
-      hipLaunchKernelGGL((decode_merge_balanced_kernel<D, false>), mgrid, dim3(64), 0, stream, a);
+      hipLaunchKernelGGL((decode_merge_balanced_kernel<D, false>), hgrid, dim3(64 * kMergeHeads), 0, stream, a);
   } else if (a.max_parts > 1) {
     if (bf16)
       hipLaunchKernelGGL((decode_merge_kernel<D, true>), mgrid, dim3(64), 0, stream, a);

@@ -293,8 +293,13 @@ int decode_impl(const pa_cache_desc* desc, void* out, const void* q, const void*
   a.nontemporal = nontemporal_mode(desc, num_seqs, max_context_len, lay.workers > 0);
   a.scale_log2 = scale * pa::kLog2e;
   if (append) {
-    if (lay.workers > 0 && desc->dtype == PA_BF16) {
-      a.new_k = new_k;  // one pass: the balanced kernel attends and stores the newest token
+    // Fused only when the requests do not outnumber the workers: then most
+    // requests are split anyway and go through the merge, which takes the newest
+    // token in. With more requests than workers most are whole, and writing
+    // their output directly (after a small store of the newest tokens) is cheaper
+    // than sending every request through the merge.
+    if (lay.workers > 0 && desc->dtype == PA_BF16 && num_seqs <= lay.workers) {
+      a.new_k = new_k;  // the merge attends and stores the newest token
       a.new_v = new_v;
     } else {
       const int row_bytes = desc->num_kv_heads * desc->head_dim * elem_bytes(desc->dtype);
