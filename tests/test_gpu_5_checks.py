@@ -104,3 +104,33 @@ def test_out_of_range_slot_without_check_is_skipped():
     assert np.array_equal(after[0, 7], su.key[1])
     after[0, 7] = before[0, 7]
     assert np.array_equal(after, before)
+
+
+def test_check_mode_decode_append(monkeypatch):
+    """Check mode validates pa_decode_append's metadata like pa_decode's: an out-of-range id in
+    the block of the newest token, or a zero length, is rejected before any launch."""
+    w = small()
+    d, k, v = gpu_pools(w, include_step=False)
+    monkeypatch.setenv("PA_CHECK", "1")
+    dec, sw = w.decode, w.step_write
+    q = device_tensor(dec.q, "bf16")
+    key, val = device_tensor(sw.key, "bf16"), device_tensor(sw.value, "bf16")
+    out = torch.empty_like(q)
+    ws = pa.decode_workspace(d, 4, 40)
+    before = host_bits(k).copy()
+    bt = dec.block_tables.copy()
+    bt[3, (33 - 1) // 16] = w.spec.num_blocks  # request 3's newest token (position 32) is in block 2
+    with pytest.raises(pa.PAError) as e:
+        pa.pa_decode_append(d, out, q, key, val, k, v, i32(bt), i32(dec.context_lens), 40, w.scale, ws)
+    assert e.value.status == RANGE
+    lens = dec.context_lens.copy()
+    lens[0] = 0
+    with pytest.raises(pa.PAError) as e:
+        pa.pa_decode_append(d, out, q, key, val, k, v, i32(dec.block_tables), i32(lens), 40, w.scale, ws)
+    assert e.value.status == RANGE
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(k), before)  # nothing was launched
+    pa.pa_decode_append(d, out, q, key, val, k, v, i32(dec.block_tables), i32(dec.context_lens), 40,
+                        w.scale, ws)
+    torch.cuda.synchronize()
+    assert np.all(np.isfinite(as64(out)))
