@@ -181,6 +181,30 @@ int pa_decode_append(const pa_cache_desc* desc, void* out, const void* q, const 
                      int32_t max_context_len, float scale, int32_t partition_tokens, void* workspace,
                      size_t workspace_bytes, void* stream);
 
+/* Decode when every request shares its first prefix_blocks blocks (the same
+ * block ids at the start of every row of block_tables, as when a common prompt
+ * is found in the prefix cache): the same result as pa_decode. The prefix is
+ * read once for all requests: its attention runs as one dense pass over all the
+ * requests' queries on the matrix cores, split into key ranges. Only each
+ * request's remaining blocks go through the split-KV decode, and the merge
+ * combines both. Sharing full blocks between requests through the prefix cache
+ * is arcyou teardown, "PagedAttention: the KV cache is paged, like virtual
+ * memory"; the result is attention over each request's whole logical context.
+ *   prefix_blocks   0 (then this is pa_decode) or the number of shared blocks;
+ *                   every context_lens[s] >= 16 * prefix_blocks
+ * bf16 pools, num_seqs <= 8192; other arguments and errors as for pa_decode.
+ * PA_CHECK=1 also verifies the lengths and that every row starts with row 0's
+ * prefix blocks. The workspace must hold
+ * pa_decode_shared_prefix_workspace_size(desc, num_seqs, max_context_len,
+ * prefix_blocks) bytes. */
+size_t pa_decode_shared_prefix_workspace_size(const pa_cache_desc* desc, int32_t num_seqs,
+                                              int32_t max_context_len, int32_t prefix_blocks);
+int pa_decode_shared_prefix(const pa_cache_desc* desc, void* out, const void* q, const void* k_cache,
+                            const void* v_cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
+                            int32_t prefix_blocks, float scale, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
 /* Copy whole blocks inside the pool, K and V alike: the copy-on-write step that
  * lets forked sequences share blocks until one of them must write into a shared
  * block, which is then duplicated first (aitrending, "The 1960s Operating System

@@ -23,6 +23,8 @@ from ._lib import (  # noqa: F401
     pa_decode,
     pa_decode_append,
     pa_decode_partition_tokens,
+    pa_decode_shared_prefix,
+    pa_decode_shared_prefix_workspace_size,
     pa_decode_workspace_size,
     pa_gather_kv,
     pa_last_error_detail,

@@ -305,10 +305,12 @@ __device__ __forceinline__ int pool_keys(const DecodeArgs& a, int s) {
   return kAppend ? L - 1 : L;
 }
 
+// Blocks of request s the balanced kernel reads: those holding its pool keys,
+// less the first skip_blocks (shared-prefix mode).
 template <bool kAppend>
 __device__ __forceinline__ int request_blocks(const DecodeArgs& a, int s) {
   const int n = pool_keys<kAppend>(a, s);
-  return n > 0 ? (n + 15) >> 4 : 0;
+  return n > 0 ? max(((n + 15) >> 4) - a.skip_blocks, 0) : 0;
 }
 
 // Balanced mode: grid (W, kv-head groups); dynamic LDS holds S+1 ints.
@@ -375,14 +377,13 @@ __global__ __launch_bounds__(64 * NW) void decode_bf16_balanced_kernel(DecodeArg
     if (ce > pos) {
       const int seg_end = min(ce, hi);
       const int n_keys = pool_keys<kAppend>(a, s);
-      const bool whole = !kAppend && pos == cs && seg_end == ce;
+      const bool whole = !kAppend && !a.partial_only && pos == cs && seg_end == ce;
       const int64_t slot = (int64_t)s + w;
+      const int b0 = a.skip_blocks + pos - cs, b1 = a.skip_blocks + seg_end - cs;  // table indices
       if (nt)
-        decode_segment<D, true>(a, s, kvh, pos - cs, seg_end - cs, n_keys, whole,
-                                slot * a.num_q_heads, 1);
+        decode_segment<D, true>(a, s, kvh, b0, b1, n_keys, whole, slot * a.num_q_heads, 1);
       else
-        decode_segment<D, false>(a, s, kvh, pos - cs, seg_end - cs, n_keys, whole,
-                                 slot * a.num_q_heads, 1);
+        decode_segment<D, false>(a, s, kvh, b0, b1, n_keys, whole, slot * a.num_q_heads, 1);
       pos = seg_end;
     }
     ++s;
@@ -395,6 +396,20 @@ __device__ __forceinline__ int worker_of(int64_t b, int64_t T, int W) {
   return (int)(((b + 1) * W + T - 1) / T) - 1;
 }
 
+// (M, den, o) of one fold combined with another's (M2, den2, o2), each relative
+// to its own maximum; either may be empty (M = -inf, den = 0, o = 0).
+template <int kE>
+__device__ __forceinline__ void combine_folds(float& M, float& den, float* o, float M2, float den2,
+                                              const float* o2) {
+  const float Mn = fmaxf(M, M2);
+  if (Mn == -INFINITY) return;  // both empty
+  const float w1 = fast_exp2(M - Mn), w2 = fast_exp2(M2 - Mn);
+  den = den * w1 + den2 * w2;
+#pragma unroll
+  for (int e = 0; e < kE; ++e) o[e] = o[e] * w1 + o2[e] * w2;
+  M = Mn;
+}
+
 // q heads merged by one workgroup of decode_merge_balanced_kernel (one wavefront
 // each): with many short requests the merge is dispatch-bound, so workgroups
 // take several heads.
@@ -405,24 +420,32 @@ constexpr int kMergeHeads = 8;
 // o = sum_i 2^(m_i - M) acc_i and den = sum_i 2^(m_i - M) l_i; the caller divides.
 // Partials are read eight at a time, all loads of a batch issued before any use,
 // and folded into a running (M, den, o) rescaled to the batch maximum.
+// Partials np .. np + np2 - 1 (when np2 > 0) come from a second list: rows
+// row2 + i of acc2 / ml2, folded in the same batches as the first list's.
 template <int D>
-__device__ __forceinline__ void fold_partials(const DecodeArgs& a, int64_t row0, int64_t rstep, int np,
-                                              int lane, float (&o)[D / 64], float& den, float& M) {
+__device__ __forceinline__ void fold_partials(const float* part_acc, const float* part_ml, int64_t row0,
+                                              int64_t rstep, int np, int lane, float (&o)[D / 64], float& den,
+                                              float& M, const float* acc2 = nullptr, const float* ml2 = nullptr,
+                                              int64_t row2 = 0, int np2 = 0) {
   constexpr int kE = D / 64;
   constexpr int kBatch = 8;
   M = -INFINITY;
   den = 0.f;
 #pragma unroll
   for (int e = 0; e < kE; ++e) o[e] = 0.f;
-  for (int i0 = 0; i0 < np; i0 += kBatch) {
+  const int n = np + np2;
+  for (int i0 = 0; i0 < n; i0 += kBatch) {
     float mi[kBatch], li[kBatch], ai[kBatch][kE];
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
-      const bool in = i0 + j < np;
-      const int64_t r = row0 + (int64_t)(in ? i0 + j : 0) * rstep;
-      mi[j] = in ? a.part_ml[2 * r] : -INFINITY;
-      li[j] = in ? a.part_ml[2 * r + 1] : 0.f;
-      const float* src = a.part_acc + r * D + kE * lane;
+      const int i = i0 + j;
+      const bool in = i < n, second = i >= np;
+      const float* ml = second ? ml2 : part_ml;
+      const float* acc = second ? acc2 : part_acc;
+      const int64_t r = !in ? row0 : second ? row2 + (i - np) : row0 + (int64_t)i * rstep;
+      mi[j] = in ? ml[2 * r] : -INFINITY;
+      li[j] = in ? ml[2 * r + 1] : 0.f;
+      const float* src = acc + r * D + kE * lane;
 #pragma unroll
       for (int e = 0; e < kE; ++e) ai[j][e] = in ? src[e] : 0.f;
     }
@@ -491,12 +514,14 @@ __global__ __launch_bounds__(64 * kMergeHeads) void decode_merge_balanced_kernel
   const int w0 = worker_of(c0, Tn, W);
   const int w1 = worker_of(max(c1 - 1, c0), Tn, W);
   const bool has_blocks = c1 > c0;  // false for L <= 0
-  if (!kAppend && L > 0 && w0 == w1) return;  // one segment: written by the decode kernel
+  if (!kAppend && !a.partial_only && L > 0 && w0 == w1) return;  // one segment: written by the decode kernel
   const int np = has_blocks ? w1 - w0 + 1 : 0;
   // partial of worker w0 + i for this (request, head) is row (s + w0 + i) * Hq + h
   const int64_t row0 = ((int64_t)s + w0) * a.num_q_heads + h;
   float o[kE], den, M;
-  fold_partials<D>(a, row0, a.num_q_heads, np, lane, o, den, M);
+  // in shared-prefix mode the prefix's partials of this (request, head) follow the tail's
+  fold_partials<D>(a.part_acc, a.part_ml, row0, a.num_q_heads, np, lane, o, den, M, a.pre_acc, a.pre_ml,
+                   ((int64_t)s * a.num_q_heads + h) * a.pre_parts, a.pre_parts);
   if constexpr (kAppend) {
     float part = 0.f;
 #pragma unroll
@@ -555,7 +580,7 @@ __global__ __launch_bounds__(256) void decode_merge_wide_kernel(DecodeArgs a) {
   const int W = (int)min((int64_t)a.num_workers, Tn);  // as in the decode kernel
   const int w0 = worker_of(c0, Tn, W);
   const int w1 = worker_of(max(c1 - 1, c0), Tn, W);
-  if (!kAppend && L > 0 && w0 == w1) return;  // one segment: written by the decode kernel
+  if (!kAppend && !a.partial_only && L > 0 && w0 == w1) return;  // one segment: written by the decode kernel
   const int np = c1 > c0 ? w1 - w0 + 1 : 0;
   const int64_t row0 = ((int64_t)s + w0) * a.num_q_heads + h;
   const int64_t rstep = a.num_q_heads;
@@ -611,6 +636,24 @@ __global__ __launch_bounds__(256) void decode_merge_wide_kernel(DecodeArgs a) {
     }
   }
   M = Mt;
+  if (a.pre_parts > 0) {  // shared-prefix mode: the prefix's partials of this (request, head)
+    const int64_t p0 = ((int64_t)s * a.num_q_heads + h) * a.pre_parts;
+    float M2 = -INFINITY, den2 = 0.f;
+    f32x4 o2 = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < a.pre_parts; ++j) {
+      const float mj = a.pre_ml[2 * (p0 + j)];
+      const float lj = a.pre_ml[2 * (p0 + j) + 1];
+      const f32x4 aj = *(const f32x4*)(a.pre_acc + (p0 + j) * D + 4 * ti);
+      const float mb = fmaxf(M2, mj);
+      const float alpha = fast_exp2(M2 - mb), wgt = fast_exp2(mj - mb);
+      den2 = den2 * alpha + wgt * lj;
+      o2 = o2 * alpha + wgt * aj;
+      M2 = mb;
+    }
+    float ov[4] = {o[0], o[1], o[2], o[3]}, ov2[4] = {o2[0], o2[1], o2[2], o2[3]};
+    combine_folds<4>(M, den, ov, M2, den2, ov2);
+    o = f32x4{ov[0], ov[1], ov[2], ov[3]};
+  }
   if constexpr (kAppend) {
     // the newest key as one more partial (m = its score, l = 1, acc = its V row)
     const int64_t nrow = ((int64_t)s * a.num_kv_heads + kvh) * D + 4 * ti;
@@ -812,7 +855,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   const int64_t base = ((int64_t)s * a.num_q_heads + h) * a.max_parts;
   float o[kE], den;
   float M;
-  fold_partials<D>(a, base, 1, nparts, lane, o, den, M);
+  fold_partials<D>(a.part_acc, a.part_ml, base, 1, nparts, lane, o, den, M);
   const float inv = 1.f / den;
   const int64_t orow = ((int64_t)s * a.num_q_heads + h) * D + kE * lane;
   if constexpr (kBf16) {

@@ -3,6 +3,7 @@
 // dispatch on the caller's stream. No device memory is allocated here.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdlib>
 #include <string>
@@ -149,6 +150,39 @@ DecodeLayout decode_layout(const pa_cache_desc* d, int32_t num_seqs, int32_t max
   return l;
 }
 
+// Shared-prefix decode: the balanced decode's workspace (for the tails), then the
+// prefix pass's partials [S][Hq][splits][D] and [S][Hq][splits][2]. The prefix
+// keys are split into ranges of whole 64-key tiles so that the prefix pass has
+// about 256 workgroups (256 packed rows of one kv head each; one per compute
+// unit): more, shorter ones paid their set-up twice and left more partials.
+struct PrefixLayout {
+  DecodeLayout dec;
+  int32_t key_chunk;
+  int32_t splits;
+  size_t acc_offset, ml_offset, total;
+};
+
+PrefixLayout prefix_layout(const pa_cache_desc* d, int32_t num_seqs, int32_t max_context_len,
+                           int32_t prefix_blocks) {
+  PrefixLayout p{};
+  p.dec = decode_layout(d, num_seqs, max_context_len, 0);
+  const int64_t keys = (int64_t)prefix_blocks * PA_BLOCK_SIZE;
+  const int64_t tiles = (keys + 63) / 64;
+  const int group = d->num_q_heads / d->num_kv_heads;
+  const int64_t row_tiles = ((int64_t)num_seqs * group + 255) / 256;
+  const int64_t wgs = (int64_t)d->num_kv_heads * row_tiles;
+  const int64_t target = std::max(1, env_int("PA_PREFIX_WORKGROUPS", 256));  // tuning override
+  int64_t splits = std::min<int64_t>(std::max<int64_t>(tiles, 1), std::max<int64_t>(1, (target + wgs - 1) / wgs));
+  const int64_t tiles_per = (tiles + splits - 1) / splits;
+  p.key_chunk = (int32_t)(64 * std::max<int64_t>(tiles_per, 1));
+  p.splits = (int32_t)std::max<int64_t>(1, (keys + p.key_chunk - 1) / p.key_chunk);
+  const size_t rows = (size_t)num_seqs * d->num_q_heads * p.splits;
+  p.acc_offset = align256(p.dec.total);
+  p.ml_offset = p.acc_offset + align256(rows * d->head_dim * sizeof(float));
+  p.total = p.ml_offset + align256(rows * 2 * sizeof(float));
+  return p;
+}
+
 // Non-temporal K/V loads: -1 lets the balanced kernel decide from the total
 // attended blocks; the fixed-partition kernel streams when no block can be read
 // twice and the pool is far larger than the 256 MiB last-level cache.
@@ -230,12 +264,13 @@ size_t pa_decode_workspace_size(const pa_cache_desc* desc, int32_t num_seqs,
 }
 
 namespace {
-// pa_decode, and pa_decode_append when new_k/new_v are given.
+// pa_decode; pa_decode_append when new_k/new_v are given; pa_decode_shared_prefix
+// when prefix_blocks > 0 (balanced bf16 mode only).
 int decode_impl(const pa_cache_desc* desc, void* out, const void* q, const void* new_k,
                 const void* new_v, const void* k_cache, const void* v_cache,
                 const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
                 int32_t num_seqs, int32_t max_context_len, float scale, int32_t partition_tokens,
-                void* workspace, size_t workspace_bytes, void* stream) {
+                void* workspace, size_t workspace_bytes, void* stream, int32_t prefix_blocks = 0) {
   int st = validate_desc(desc);
   if (st != PA_OK) return st;
   if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs is negative");
@@ -253,9 +288,19 @@ int decode_impl(const pa_cache_desc* desc, void* out, const void* q, const void*
   if (partition_tokens < 0 || partition_tokens % PA_BLOCK_SIZE != 0)
     return fail(PA_ERR_INVALID_ARG, "partition_tokens must be 0 or a positive multiple of 16");
   if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
-  const DecodeLayout lay = decode_layout(desc, num_seqs, max_context_len, partition_tokens);
-  if (lay.total > 0 && (workspace == nullptr || workspace_bytes < lay.total))
-    return fail(PA_ERR_WORKSPACE, "workspace needs " + std::to_string(lay.total) + " bytes");
+  const bool prefix = prefix_blocks > 0;
+  if (prefix) {
+    if (desc->dtype != PA_BF16) return fail(PA_ERR_UNSUPPORTED, "a shared prefix needs a bf16 pool");
+    if (num_seqs > pa::decode_max_balanced_seqs())
+      return fail(PA_ERR_UNSUPPORTED, "a shared prefix needs at most 8192 requests");
+    if ((int64_t)prefix_blocks * PA_BLOCK_SIZE > max_context_len)
+      return fail(PA_ERR_INVALID_ARG, "prefix_blocks exceeds max_context_len / 16");
+  }
+  const PrefixLayout play = prefix_layout(desc, num_seqs, max_context_len, prefix ? prefix_blocks : 0);
+  const DecodeLayout lay = prefix ? play.dec : decode_layout(desc, num_seqs, max_context_len, partition_tokens);
+  const size_t need = prefix ? play.total : lay.total;
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(PA_ERR_WORKSPACE, "workspace needs " + std::to_string(need) + " bytes");
   if (check_mode()) {
     if (hipStreamSynchronize(as_stream(stream)) != hipSuccess)
       return fail(PA_ERR_HIP, "stream synchronize failed");
@@ -269,6 +314,14 @@ int decode_impl(const pa_cache_desc* desc, void* out, const void* q, const void*
                                       std::to_string(lens[s]) + " is outside [1, max_context_len]");
     st = check_tables(tables, max_blocks_per_seq, lens, desc->num_blocks);
     if (st != PA_OK) return st;
+    for (int s = 0; prefix && s < num_seqs; ++s) {
+      if (lens[s] < prefix_blocks * PA_BLOCK_SIZE)
+        return fail(PA_ERR_RANGE, "context_lens[" + std::to_string(s) + "] is shorter than the shared prefix");
+      for (int b = 0; b < prefix_blocks; ++b)
+        if (tables[(size_t)s * max_blocks_per_seq + b] != tables[b])
+          return fail(PA_ERR_RANGE, "block_tables[" + std::to_string(s) + "][" + std::to_string(b) +
+                                        "] differs from the shared prefix of row 0");
+    }
   }
   pa::DecodeArgs a{};
   a.q = q;
@@ -292,6 +345,34 @@ int decode_impl(const pa_cache_desc* desc, void* out, const void* q, const void*
   a.num_workers = lay.workers;
   a.nontemporal = nontemporal_mode(desc, num_seqs, max_context_len, lay.workers > 0);
   a.scale_log2 = scale * pa::kLog2e;
+  if (prefix) {
+    // the prefix once for all requests (MFMA, keys split into ranges), then the
+    // tails through the balanced decode, both as partials for the merge
+    pa::PrefillArgs pf{};
+    pf.q = (const uint16_t*)q;
+    pf.k = (const uint16_t*)k_cache;
+    pf.v = (const uint16_t*)v_cache;
+    pf.block_tables = block_tables;
+    pf.num_blocks = desc->num_blocks;
+    pf.max_blocks = max_blocks_per_seq;
+    pf.num_seqs = num_seqs;
+    pf.num_q_heads = desc->num_q_heads;
+    pf.num_kv_heads = desc->num_kv_heads;
+    pf.scale_log2 = a.scale_log2;
+    pf.prefix_keys = prefix_blocks * PA_BLOCK_SIZE;
+    pf.key_chunk = play.key_chunk;
+    pf.key_splits = play.splits;
+    pf.part_acc = (float*)((char*)workspace + play.acc_offset);
+    pf.part_ml = (float*)((char*)workspace + play.ml_offset);
+    st = hip_status(pa::launch_prefix_attention(pf, desc->head_dim, a.group, as_stream(stream)),
+                    "prefix launch");
+    if (st != PA_OK) return st;
+    a.skip_blocks = prefix_blocks;
+    a.partial_only = 1;
+    a.pre_parts = play.splits;
+    a.pre_acc = pf.part_acc;
+    a.pre_ml = pf.part_ml;
+  }
   if (append) {
     // Fused only when the requests do not outnumber the workers: then most
     // requests are split anyway and go through the merge, which takes the newest
@@ -323,6 +404,24 @@ int pa_decode(const pa_cache_desc* desc, void* out, const void* q, const void* k
   return decode_impl(desc, out, q, nullptr, nullptr, k_cache, v_cache, block_tables, max_blocks_per_seq,
                      context_lens, num_seqs, max_context_len, scale, partition_tokens, workspace,
                      workspace_bytes, stream);
+}
+
+size_t pa_decode_shared_prefix_workspace_size(const pa_cache_desc* desc, int32_t num_seqs,
+                                              int32_t max_context_len, int32_t prefix_blocks) {
+  if (validate_desc(desc) != PA_OK || num_seqs <= 0 || max_context_len <= 0 || prefix_blocks < 0) return 0;
+  if (prefix_blocks == 0) return decode_layout(desc, num_seqs, max_context_len, 0).total;
+  return prefix_layout(desc, num_seqs, max_context_len, prefix_blocks).total;
+}
+
+int pa_decode_shared_prefix(const pa_cache_desc* desc, void* out, const void* q, const void* k_cache,
+                            const void* v_cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
+                            int32_t prefix_blocks, float scale, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  if (prefix_blocks < 0) return fail(PA_ERR_INVALID_ARG, "prefix_blocks is negative");
+  return decode_impl(desc, out, q, nullptr, nullptr, k_cache, v_cache, block_tables, max_blocks_per_seq,
+                     context_lens, num_seqs, max_context_len, scale, 0, workspace, workspace_bytes, stream,
+                     prefix_blocks);
 }
 
 int pa_decode_append(const pa_cache_desc* desc, void* out, const void* q, const void* key,

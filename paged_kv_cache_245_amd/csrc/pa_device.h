@@ -101,6 +101,15 @@ struct DecodeArgs {
   // and stores it into its slot through the block table.
   const void* new_k;
   const void* new_v;
+  // Shared-prefix mode (balanced only): every request's first skip_blocks blocks
+  // are not read; every segment leaves a partial (partial_only); and the merge
+  // also folds pre_parts partials per (request, q head) from pre_acc / pre_ml
+  // (laid out as PrefillArgs' part_acc / part_ml).
+  int32_t skip_blocks;
+  int32_t partial_only;
+  int32_t pre_parts;
+  const float* pre_acc;
+  const float* pre_ml;
 };
 
 struct PrefillArgs {
@@ -120,6 +129,16 @@ struct PrefillArgs {
   int32_t num_q_heads;
   int32_t num_kv_heads;
   float scale_log2;
+  // Shared-prefix mode (launch_prefix_attention): the rows are the decode
+  // queries q [num_seqs][Hq][D], all attending the first prefix_keys keys of
+  // block table row 0 with no causal mask; the keys are split into key_splits
+  // ranges of key_chunk (a multiple of 64), and each (request, q head, range)
+  // leaves a partial (m, l, acc) instead of an output.
+  int32_t prefix_keys;
+  int32_t key_chunk;
+  int32_t key_splits;
+  float* part_acc;  // [num_seqs][Hq][key_splits][D]
+  float* part_ml;   // [num_seqs][Hq][key_splits][2]
 };
 
 hipError_t launch_write_kv(const void* key, const void* value, void* k_cache, void* v_cache,
@@ -138,6 +157,7 @@ int decode_waves(int num_kv_heads);
 // most requests the balanced decode mode accepts (block prefix sums live in LDS)
 int decode_max_balanced_seqs();
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int group, hipStream_t stream);
+hipError_t launch_prefix_attention(const PrefillArgs& a, int head_dim, int group, hipStream_t stream);
 hipError_t launch_gather_kv(void* dst_k, void* dst_v, const void* k_cache, const void* v_cache,
                             const int32_t* block_tables, int32_t max_blocks,
                             const int32_t* context_lens, int32_t num_seqs,

@@ -181,7 +181,7 @@ __device__ void item_of_rank(const PrefillArgs& a, int64_t rank, int kPos, int l
   }
 }
 
-template <int D, int G>
+template <int D, int G, bool kCross>
 __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a) {
   static_assert(D == 64 || D == 128, "head_dim");
   constexpr int kPos = kRows / G;            // query positions per workgroup
@@ -198,34 +198,51 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int Hkv = a.num_kv_heads;
-  __shared__ int item[3];  // this workgroup's (request, kv head, query tile)
-  if (wave == 0) {
-    int mine[3];
-    item_of_rank(a, blockIdx.x + (int64_t)gridDim.x * blockIdx.y, kPos, lane, mine);
-    if (lane == 0) {
-      item[0] = mine[0];
-      item[1] = mine[1];
-      item[2] = mine[2];
+  // the workgroup's (request, kv head, query tile) and, in shared-prefix mode,
+  // its range [k_lo, L) of prefix keys
+  int s, kvh, tile, q0, nq, L, k_lo = 0;
+  bool poisoned = false;
+  if constexpr (kCross) {
+    // Shared-prefix mode: the rows are the decode queries of the num_seqs requests
+    // (one position each), and every row attends keys [k_lo, L) of the prefix that
+    // all requests share, read through block table row 0, with no causal mask.
+    s = 0;
+    kvh = blockIdx.x % Hkv;
+    tile = blockIdx.x / Hkv;
+    q0 = 0;
+    nq = a.num_seqs;
+    k_lo = blockIdx.y * a.key_chunk;
+    L = min(k_lo + a.key_chunk, a.prefix_keys);
+    if (tile * kPos >= nq || k_lo >= L) return;  // uniform over the workgroup
+  } else {
+    __shared__ int item[3];  // this workgroup's (request, kv head, query tile)
+    if (wave == 0) {
+      int mine[3];
+      item_of_rank(a, blockIdx.x + (int64_t)gridDim.x * blockIdx.y, kPos, lane, mine);
+      if (lane == 0) {
+        item[0] = mine[0];
+        item[1] = mine[1];
+        item[2] = mine[2];
+      }
     }
+    __syncthreads();
+    s = item[0];
+    if (s < 0) return;  // uniform: more workgroups than items
+    kvh = item[1];
+    tile = item[2];
+    q0 = a.query_start_loc[s];
+    nq = a.query_start_loc[s + 1] - q0;
+    L = a.seq_lens[s];
+    nq = min(nq, a.max_query_len);
+    nq = min(nq, a.num_tokens - q0);
+    L = min(L, a.max_seq_len);
+    L = min(L, a.max_blocks * 16);
+    if (q0 < 0 || tile * kPos >= nq) return;  // uniform over the workgroup
+    // A chunk longer than its context is inconsistent: stay in bounds, output NaN.
+    poisoned = L < nq;
   }
-  __syncthreads();
-  const int s = item[0];
-  if (s < 0) return;  // uniform: more workgroups than items
-  const int kvh = item[1];
-  const int tile = item[2];
-
-  const int q0 = a.query_start_loc[s];
-  int nq = a.query_start_loc[s + 1] - q0;
-  int L = a.seq_lens[s];
-  nq = min(nq, a.max_query_len);
-  nq = min(nq, a.num_tokens - q0);
-  L = min(L, a.max_seq_len);
-  L = min(L, a.max_blocks * 16);
   const int pos0 = tile * kPos;
-  if (q0 < 0 || pos0 >= nq) return;  // uniform over the workgroup
-  // A chunk longer than its context is inconsistent: stay in bounds, output NaN.
-  bool poisoned = L < nq;
-  const int cached = max(L - nq, 0);
+  const int cached = kCross ? 0 : max(L - nq, 0);
 
   const int col = lane & 31;
   const int half = lane >> 5;
@@ -241,10 +258,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
     qb[c] = row_ok ? *(const u32x4*)(a.q + qrow + 16 * c + 8 * half) : u32x4{0, 0, 0, 0};
 
   const float c_log2 = a.scale_log2;
-  const int row_limit = cached + pos;                // last key this row sees
-  const int kv_end = cached + min(pos0 + kPos, nq);  // keys the workgroup needs
-  const int first_limit = cached + pos0;             // smallest row limit in the workgroup
+  // last key this row sees, keys the workgroup needs, smallest row limit in it
+  const int row_limit = kCross ? L - 1 : cached + pos;
+  const int kv_end = kCross ? L : cached + min(pos0 + kPos, nq);
+  const int first_limit = kCross ? L - 1 : cached + pos0;
   const int n_tiles = (kv_end + kBN - 1) / kBN;
+  const int t0 = k_lo / kBN;  // first tile (k_lo is a multiple of kBN)
   const int32_t* table = a.block_tables + (int64_t)s * a.max_blocks;
   const int nblocks = (L + 15) >> 4;
   const int64_t block_elems = (int64_t)kBlock * Hkv * D;
@@ -265,7 +284,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
     src_off[i] = (row & 15) * row_elems + kvh * D + 8 * ch;
   }
   // block ids this wavefront copies, 64 tiles at a time: lane j holds tile id_tile0 + j
-  int id_tile0 = 0;
+  int id_tile0 = t0;
   auto fetch_ids = [&]() {
     const int blk = 4 * (id_tile0 + lane) + sblk;
     return blk < nblocks ? table[blk] : 0;
@@ -324,8 +343,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
     (&Vs[0][0])[i] = u32x4{0, 0, 0, 0};
   }
   __syncthreads();
-  stage_load(0, 0);
-  if (n_tiles > 1) stage_load(1, 1);
+  stage_load(t0, 0);
+  if (t0 + 1 < n_tiles) stage_load(t0 + 1, 1);
   // both tiles landed (a partial count would not do: rows past the context skip
   // their loads) and are visible to every wavefront
   __builtin_amdgcn_s_waitcnt(0);
@@ -444,7 +463,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
     __syncthreads();
     if (t + 2 < n_tiles) stage_load(t + 2, buf);
   };
-  for (int t = 0; t < n_tiles; t += 2) {
+  for (int t = t0; t < n_tiles; t += 2) {
     tile_step(t, std::integral_constant<int, 0>{});
     if (t + 1 < n_tiles) tile_step(t + 1, std::integral_constant<int, 1>{});
   }
@@ -452,6 +471,22 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
   poisoned = __syncthreads_or(poisoned);
   lsum += __shfl_xor(lsum, 32, 64);
   if (!row_ok) return;
+  if constexpr (kCross) {
+    // partial (m, l, acc) of row (request pos, q head h) over key range blockIdx.y
+    const int64_t pidx = ((int64_t)pos * a.num_q_heads + h) * a.key_splits + blockIdx.y;
+    float* dst = a.part_acc + pidx * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int grp = 0; grp < 4; ++grp)  // o[dt][4 grp + i] is dim 32 dt + 8 grp + 4 half + i
+        *(f32x4*)(dst + 32 * dt + 8 * grp + 4 * half) =
+            f32x4{o[dt][4 * grp], o[dt][4 * grp + 1], o[dt][4 * grp + 2], o[dt][4 * grp + 3]};
+    if (half == 0) {
+      a.part_ml[2 * pidx] = m;
+      a.part_ml[2 * pidx + 1] = poisoned ? __builtin_nanf("") : lsum;
+    }
+    return;
+  }
   const float inv = poisoned ? __builtin_nanf("") : 1.f / lsum;
   uint16_t* orow = a.out + qrow;
 #pragma unroll
@@ -467,22 +502,28 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
   }
 }
 
-template <int D, int G>
+template <int D, int G, bool kCross>
 hipError_t launch_dg(const PrefillArgs& a, hipStream_t stream) {
   constexpr int kPos = kRows / G;
-  dim3 grid(a.num_seqs * a.num_kv_heads, (a.max_query_len + kPos - 1) / kPos);
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, G>), grid, dim3(kThreads), 0, stream, a);
+  if constexpr (kCross) {
+    // (query tile, kv head) pairs along x, key ranges along y
+    dim3 grid(a.num_kv_heads * ((a.num_seqs + kPos - 1) / kPos), a.key_splits);
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, G, true>), grid, dim3(kThreads), 0, stream, a);
+  } else {
+    dim3 grid(a.num_seqs * a.num_kv_heads, (a.max_query_len + kPos - 1) / kPos);
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, G, false>), grid, dim3(kThreads), 0, stream, a);
+  }
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool kCross>
 hipError_t launch_d(const PrefillArgs& a, int group, hipStream_t stream) {
   switch (group) {
-    case 1: return launch_dg<D, 1>(a, stream);
-    case 2: return launch_dg<D, 2>(a, stream);
-    case 4: return launch_dg<D, 4>(a, stream);
-    case 8: return launch_dg<D, 8>(a, stream);
-    case 16: return launch_dg<D, 16>(a, stream);
+    case 1: return launch_dg<D, 1, kCross>(a, stream);
+    case 2: return launch_dg<D, 2, kCross>(a, stream);
+    case 4: return launch_dg<D, 4, kCross>(a, stream);
+    case 8: return launch_dg<D, 8, kCross>(a, stream);
+    case 16: return launch_dg<D, 16, kCross>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -490,8 +531,13 @@ hipError_t launch_d(const PrefillArgs& a, int group, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int group, hipStream_t stream) {
-  if (head_dim == 128) return launch_d<128>(a, group, stream);
-  return launch_d<64>(a, group, stream);
+  if (head_dim == 128) return launch_d<128, false>(a, group, stream);
+  return launch_d<64, false>(a, group, stream);
+}
+
+hipError_t launch_prefix_attention(const PrefillArgs& a, int head_dim, int group, hipStream_t stream) {
+  if (head_dim == 128) return launch_d<128, true>(a, group, stream);
+  return launch_d<64, true>(a, group, stream);
 }
 
 }  // namespace pa

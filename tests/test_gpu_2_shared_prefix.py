@@ -1,0 +1,121 @@
+"""Decode with a prefix shared by every request (pa_decode_shared_prefix) against the oracle.
+
+The shared prefix is attended once for all requests (MFMA, split into key ranges),
+the tails through the split-KV decode, and the merge combines both; the result
+must be the oracle's plain decode over each request's whole context.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_245_amd as pa
+import workloads
+from gpu_support import as64, assert_close, device_tensor, gpu_pools, host_bits, i32, run_decode, say
+from oracle_support import oracle_decode, oracle_pools
+
+pytestmark = pytest.mark.gpu
+RANGE = -4
+
+
+def run_shared(w, d, k, v, prefix_blocks, lens=None, tables=None):
+    dec = w.decode
+    S = len(dec.context_lens)
+    lens = dec.context_lens if lens is None else lens
+    tables = dec.block_tables if tables is None else tables
+    q = device_tensor(dec.q, w.spec.dtype)
+    out = torch.empty_like(q)
+    n = pa.pa_decode_shared_prefix_workspace_size(d, S, dec.max_context_len, prefix_blocks)
+    ws = torch.empty(max(n, 1), dtype=torch.uint8, device="cuda")
+    pa.pa_decode_shared_prefix(d, out, q, k, v, i32(tables), i32(lens), dec.max_context_len, prefix_blocks,
+                               w.scale, ws)
+    torch.cuda.synchronize()
+    return out
+
+
+def check(w, prefix_blocks, what):
+    d, k, v = gpu_pools(w)
+    out = run_shared(w, d, k, v, prefix_blocks)
+    ok, ov = oracle_pools(w)
+    assert_close(as64(out), oracle_decode(w, ok, ov), w.spec.dtype, what)
+    return d, k, v, out
+
+
+def test_prefix_shared_config():
+    """256 requests behind one 2,048-token prefix (128 shared blocks), tails of 64-512 tokens."""
+    say("  shared-prefix decode, config 3")
+    w = workloads.make(3)
+    check(w, w.shared_prefix_tokens // 16, "config 3, shared prefix")
+
+
+@pytest.mark.parametrize("group,D", [(g, D) for g in (1, 2, 4, 8, 16) for D in (64, 128)])
+def test_shapes(group, D):
+    """A 5-block (80-key) prefix: its last key range ends inside a 64-key tile."""
+    lens = [81, 82, 95, 96, 97, 150, 400, 1100]
+    w = workloads.custom_decode(400 + group + D, lens, Hq=2 * group, Hkv=2, D=D, dtype="bf16",
+                                shared_prefix_tokens=80)
+    check(w, 5, f"G={group} D={D}")
+
+
+@pytest.mark.parametrize("prefix_blocks", [1, 3, 8])
+def test_part_of_the_shared_blocks(prefix_blocks):
+    """Declaring fewer blocks than are shared is valid: the rest count as tail."""
+    w = workloads.custom_decode(77, [130, 140, 200, 700], Hq=8, Hkv=2, D=128, dtype="bf16",
+                                shared_prefix_tokens=128)
+    check(w, prefix_blocks, f"{prefix_blocks} of 8 shared blocks")
+
+
+def test_many_requests_and_key_ranges():
+    """600 requests (several query tiles per kv head) and a prefix long enough for several key
+    ranges."""
+    say("  shared-prefix decode, 600 requests")
+    lens = np.random.default_rng(5).integers(1025, 1300, 600).tolist()
+    w = workloads.custom_decode(78, lens, Hq=16, Hkv=4, D=128, dtype="bf16", shared_prefix_tokens=1024)
+    check(w, 64, "600 requests")
+
+
+def test_few_requests_long_prefix():
+    """Two requests behind an 8,192-token prefix: the prefix is split into many key ranges."""
+    w = workloads.custom_decode(79, [8200, 8500], Hq=32, Hkv=8, D=128, dtype="bf16", shared_prefix_tokens=8192)
+    check(w, 512, "2 requests, 8192-token prefix")
+
+
+def test_empty_tail_and_zero_prefix():
+    """A context that ends exactly at the prefix (no tail blocks), and prefix_blocks = 0 (plain decode)."""
+    w = workloads.custom_decode(80, [65, 70, 200], Hq=8, Hkv=2, D=64, dtype="bf16", shared_prefix_tokens=64)
+    d, k, v = gpu_pools(w)
+    ok, ov = oracle_pools(w)
+    dec = w.decode
+    lens = dec.context_lens.copy()
+    lens[0] = 64  # the whole context is the prefix
+    out = run_shared(w, d, k, v, 4, lens=lens)
+    ref = oracle.decode(dec.q, ok, ov, dec.block_tables, lens, "bf16", w.scale)
+    assert_close(as64(out), ref, "bf16", "empty tail")
+    out0 = run_shared(w, d, k, v, 0)
+    assert np.array_equal(host_bits(out0), host_bits(run_decode(w, d, k, v)))
+
+
+def test_matches_plain_decode():
+    w = workloads.c3_prefix_shared(seed=12, num_seqs=40)
+    d, k, v, out = check(w, w.shared_prefix_tokens // 16, "40 requests")
+    plain = as64(run_decode(w, d, k, v))
+    assert np.max(np.abs(as64(out) - plain)) <= 2e-2
+
+
+def test_check_mode(monkeypatch):
+    w = workloads.custom_decode(81, [70, 90, 100], Hq=8, Hkv=2, D=128, dtype="bf16", shared_prefix_tokens=64)
+    d, k, v = gpu_pools(w)
+    monkeypatch.setenv("PA_CHECK", "1")
+    dec = w.decode
+    tables = dec.block_tables.copy()
+    tables[2, 1] = tables[0, -1]  # row 0's padding (a spare block): row 2 leaves the prefix
+    with pytest.raises(pa.PAError) as e:
+        run_shared(w, d, k, v, 4, tables=tables)
+    assert e.value.status == RANGE
+    lens = dec.context_lens.copy()
+    lens[1] = 63
+    with pytest.raises(pa.PAError) as e:
+        run_shared(w, d, k, v, 4, lens=lens)
+    assert e.value.status == RANGE
+    out = run_shared(w, d, k, v, 4)
+    assert np.all(np.isfinite(as64(out)))
