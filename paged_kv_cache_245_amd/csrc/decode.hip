@@ -420,9 +420,9 @@ constexpr int kMergeHeads = 8;
 // o = sum_i 2^(m_i - M) acc_i and den = sum_i 2^(m_i - M) l_i; the caller divides.
 // Partials are read eight at a time, all loads of a batch issued before any use,
 // and folded into a running (M, den, o) rescaled to the batch maximum.
-// Partials np .. np + np2 - 1 (when np2 > 0) come from a second list: rows
-// row2 + i of acc2 / ml2, folded in the same batches as the first list's.
-template <int D>
+// kTwo: partials np .. np + np2 - 1 come from a second list, rows row2 + i of
+// acc2 / ml2, folded in the same batches as the first list's.
+template <int D, bool kTwo = false>
 __device__ __forceinline__ void fold_partials(const float* part_acc, const float* part_ml, int64_t row0,
                                               int64_t rstep, int np, int lane, float (&o)[D / 64], float& den,
                                               float& M, const float* acc2 = nullptr, const float* ml2 = nullptr,
@@ -433,13 +433,13 @@ __device__ __forceinline__ void fold_partials(const float* part_acc, const float
   den = 0.f;
 #pragma unroll
   for (int e = 0; e < kE; ++e) o[e] = 0.f;
-  const int n = np + np2;
+  const int n = kTwo ? np + np2 : np;
   for (int i0 = 0; i0 < n; i0 += kBatch) {
     float mi[kBatch], li[kBatch], ai[kBatch][kE];
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
       const int i = i0 + j;
-      const bool in = i < n, second = i >= np;
+      const bool in = i < n, second = kTwo && i >= np;
       const float* ml = second ? ml2 : part_ml;
       const float* acc = second ? acc2 : part_acc;
       const int64_t r = !in ? row0 : second ? row2 + (i - np) : row0 + (int64_t)i * rstep;
@@ -519,9 +519,11 @@ __global__ __launch_bounds__(64 * kMergeHeads) void decode_merge_balanced_kernel
   // partial of worker w0 + i for this (request, head) is row (s + w0 + i) * Hq + h
   const int64_t row0 = ((int64_t)s + w0) * a.num_q_heads + h;
   float o[kE], den, M;
-  // in shared-prefix mode the prefix's partials of this (request, head) follow the tail's
-  fold_partials<D>(a.part_acc, a.part_ml, row0, a.num_q_heads, np, lane, o, den, M, a.pre_acc, a.pre_ml,
-                   ((int64_t)s * a.num_q_heads + h) * a.pre_parts, a.pre_parts);
+  if (a.pre_parts > 0)  // shared-prefix mode: the prefix's partials of this (request, head) follow the tail's
+    fold_partials<D, true>(a.part_acc, a.part_ml, row0, a.num_q_heads, np, lane, o, den, M, a.pre_acc, a.pre_ml,
+                           ((int64_t)s * a.num_q_heads + h) * a.pre_parts, a.pre_parts);
+  else
+    fold_partials<D>(a.part_acc, a.part_ml, row0, a.num_q_heads, np, lane, o, den, M);
   if constexpr (kAppend) {
     float part = 0.f;
 #pragma unroll

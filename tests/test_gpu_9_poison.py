@@ -83,3 +83,26 @@ def test_prefill(D):
     d, kp, vp = gpu_pools(w)
     _, kz, vz = zero_pools(w)
     same_bits(run_prefill(w, d, kp, vp), run_prefill(w, d, kz, vz), "prefill")
+
+
+def test_decode_shared_prefix():
+    """The prefix pass and the tails, with a prefix that ends inside a 64-key tile."""
+    say("  poison vs zeros: decode_shared_prefix")
+    w = workloads.custom_decode(94, [81, 95, 96, 130, 700], Hq=8, Hkv=2, D=128, dtype="bf16",
+                                shared_prefix_tokens=80)
+    dec = w.decode
+
+    def run(k, v):
+        d = desc_of(w)
+        q = device_tensor(dec.q, "bf16")
+        out = torch.empty_like(q)
+        n = pa.pa_decode_shared_prefix_workspace_size(d, len(dec.context_lens), dec.max_context_len, 5)
+        ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+        pa.pa_decode_shared_prefix(d, out, q, k, v, i32(dec.block_tables), i32(dec.context_lens),
+                                   dec.max_context_len, 5, w.scale, ws)
+        torch.cuda.synchronize()
+        return out
+
+    _, kp, vp = gpu_pools(w)
+    _, kz, vz = zero_pools(w)
+    same_bits(run(kp, vp), run(kz, vz), "decode_shared_prefix")
