@@ -82,3 +82,15 @@ def test_decode_occupancy(remarks):
         nw = int(m.group(2))
         assert r["Occupancy"] >= (2 if nw == 8 else 1), (name, r)
     assert seen >= 16
+
+
+def test_prefill_occupancy(remarks):
+    """The prefill kernels (causal and shared-prefix) run 8 wavefronts per workgroup, two per
+    SIMD; their register use must leave room for that."""
+    seen = 0
+    for name, r in remarks["prefill.hip"].items():
+        if "prefill_bf16_kernel" not in name:
+            continue
+        seen += 1
+        assert r["Occupancy"] >= 2, (name, r)
+    assert seen >= 20  # {64, 128} x {1, 2, 4, 8, 16} x {causal, shared prefix}
