@@ -61,7 +61,7 @@ typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
 typedef enum {
   PA_OK = 0,
   PA_ERR_INVALID_ARG = -1, /* null pointer, non-positive size, inconsistent sizes */
-  PA_ERR_UNSUPPORTED = -2, /* shape or dtype this build has no kernel for */
+  PA_ERR_UNSUPPORTED = -2, /* shape or dtype the library has no kernel for */
   PA_ERR_WORKSPACE = -3,   /* decode workspace missing or too small */
   PA_ERR_RANGE = -4,       /* check mode found metadata outside its range */
   PA_ERR_HIP = -5          /* the HIP runtime reported an error */
