@@ -297,6 +297,12 @@ __device__ __forceinline__ void decode_segment(const DecodeArgs& a, int s, int k
     store_partial<D>(a, pidx_base + (int64_t)h * pidx_stride, acc, m, lsum, g4);
 }
 
+// Worker holding global block b when T >= W blocks are split over W workers
+// (worker w owns blocks [w*T/W, (w+1)*T/W), never an empty range).
+__device__ __forceinline__ int worker_of(int64_t b, int64_t T, int W) {
+  return (int)(((b + 1) * W + T - 1) / T) - 1;
+}
+
 // Keys of request s that the balanced kernel reads from the pool: all of its
 // context, or in append mode all but the newest token (the merge attends that one).
 template <bool kAppend>
@@ -348,17 +354,30 @@ __global__ __launch_bounds__(64 * NW) void decode_bf16_balanced_kernel(DecodeArg
   }
   if (tid == kThreads - 1) cum[S] = run;
   __syncthreads();
-  if (blockIdx.x == 0 && blockIdx.y == 0)
+  if (blockIdx.x == 0 && blockIdx.y == 0) {
     for (int r = tid; r <= S; r += kThreads) a.cum_blocks[r] = cum[r];
+    // A request with no key has no segment, and a merge over split requests only
+    // does not visit it: its output (NaN, as the merge would give) is written here.
+    if (a.merge_splits) {
+      for (int r = r0; r < r1; ++r) {
+        if (a.context_lens[r] > 0) continue;
+        uint16_t* o = (uint16_t*)a.out + (int64_t)r * a.num_q_heads * D;
+        for (int e = 0; e < a.num_q_heads * D; ++e) o[e] = 0x7FC0u;  // bf16 quiet NaN
+      }
+    }
+  }
 
   // Split over W = min(workgroups, T) workers, so that every worker owns at least
   // one block (the merge relies on it); surplus workgroups idle.
   const int64_t T = cum[S];
   const int W = (int)min((int64_t)gridDim.x, T), w = blockIdx.x;
-  if (w >= W) return;
+  const bool recorder = blockIdx.y == 0 && tid == 0 && a.split_req != nullptr;
+  if (w >= W) {
+    if (recorder) a.split_req[w] = -1;
+    return;
+  }
   const int lo = (int)((int64_t)w * T / W), hi = (int)((int64_t)(w + 1) * T / W);
   const int kvh = blockIdx.y * NW + wave;
-  if (lo >= hi || kvh >= a.num_kv_heads) return;  // no barrier after this point
 
   // first request whose blocks reach past lo
   int first = 0, last = S - 1;
@@ -366,6 +385,12 @@ __global__ __launch_bounds__(64 * NW) void decode_bf16_balanced_kernel(DecodeArg
     const int mid = (first + last) >> 1;
     if (cum[mid + 1] > lo) last = mid; else first = mid + 1;
   }
+  // A request is split when a cut between workers falls inside it; it is recorded
+  // by the worker after its first cut only, so the merge can run over the split
+  // requests alone (W <= T: every worker's range is non-empty).
+  if (recorder)
+    a.split_req[w] = (lo > cum[first] && worker_of(cum[first], T, W) == w - 1) ? first : -1;
+  if (lo >= hi || kvh >= a.num_kv_heads) return;  // no barrier after this point
   // More attended blocks than the pool holds means blocks are shared (prefix
   // sharing): keep them cacheable. Otherwise stream K/V past the caches.
   const bool nt = a.nontemporal >= 0 ? a.nontemporal != 0 : T <= a.num_blocks;
@@ -388,12 +413,6 @@ __global__ __launch_bounds__(64 * NW) void decode_bf16_balanced_kernel(DecodeArg
     }
     ++s;
   }
-}
-
-// Worker holding global block b when T >= W blocks are split over W workers
-// (worker w owns blocks [w*T/W, (w+1)*T/W), never an empty range).
-__device__ __forceinline__ int worker_of(int64_t b, int64_t T, int W) {
-  return (int)(((b + 1) * W + T - 1) / T) - 1;
 }
 
 // (M, den, o) of one fold combined with another's (M2, den2, o2), each relative
@@ -479,8 +498,11 @@ __global__ __launch_bounds__(64 * kMergeHeads) void decode_merge_balanced_kernel
   constexpr int kE = D / 64;
   const int lane = threadIdx.x & 63;
   const int h = blockIdx.x * kMergeHeads + (threadIdx.x >> 6);  // one wavefront per q head
-  const int s = blockIdx.y;
   if (h >= a.num_q_heads) return;  // whole wavefront; the kernel has no barrier
+  // grid over requests, or (many more requests than workers) over the workers'
+  // records of split requests: most requests are then whole and need no merge
+  const int s = a.merge_splits ? a.split_req[blockIdx.y] : (int)blockIdx.y;
+  if (s < 0) return;
   uint16_t* O = (uint16_t*)a.out;
   const int64_t orow = ((int64_t)s * a.num_q_heads + h) * D + kE * lane;
   // The kernel is a short chain of dependent loads, so it is written without
@@ -555,29 +577,44 @@ __global__ __launch_bounds__(64 * kMergeHeads) void decode_merge_balanced_kernel
 }
 
 // Balanced mode merge for requests split over many workers (many partials each):
-// 256 threads per (q head, request). Groups of D/4 threads own 4 dims each;
-// group g folds partials g, g + kG, g + 2 kG, ... (kG = 256 / (D/4) groups), so a
-// request split over hundreds of workers costs a few rounds of loads instead of
-// one round per eight partials. The group results are combined through LDS, and
-// group 0 finishes as decode_merge_balanced_kernel does (newest token included
-// in append mode).
+// kWideThreads threads per (q head, request). Groups of D/4 threads own 4 dims
+// each; group g folds partials g, g + kG, g + 2 kG, ... (kG = kWideThreads /
+// (D/4) groups), so a request split over 256 workers costs one round of loads
+// (eight partials per group) instead of one round per eight partials. The group
+// results are combined through LDS, and group 0 finishes as
+// decode_merge_balanced_kernel does (newest token included in append mode).
+// As there, every load that does not depend on another (the request's length
+// and block prefix sums, and in append mode the newest token's q, K, V and
+// block id) is requested first.
+constexpr int kWideThreads = 1024;
+
 template <int D, bool kAppend>
-__global__ __launch_bounds__(256) void decode_merge_wide_kernel(DecodeArgs a) {
-  constexpr int kT = D / 4;     // threads per group, one float4 of dims each
-  constexpr int kG = 256 / kT;  // groups
-  constexpr int kBatch = 16;    // partials per group and round, all loads issued first
+__global__ __launch_bounds__(kWideThreads) void decode_merge_wide_kernel(DecodeArgs a) {
+  constexpr int kT = D / 4;              // threads per group, one float4 of dims each
+  constexpr int kG = kWideThreads / kT;  // groups
+  constexpr int kBatch = 8;              // partials per group and round, all loads issued first
   const int tid = threadIdx.x;
   const int grp = tid / kT, ti = tid % kT;
   const int h = blockIdx.x;
   const int s = blockIdx.y;
   uint16_t* O = (uint16_t*)a.out;
   const int64_t orow = ((int64_t)s * a.num_q_heads + h) * D + 4 * ti;
-  // first round of loads, as in decode_merge_balanced_kernel
   const int L = min(a.context_lens[s], a.max_context_len);
   const int64_t T = a.cum_blocks[a.num_seqs];
   const int64_t c0 = a.cum_blocks[s], c1 = a.cum_blocks[s + 1];
   const int kvh = h / a.group;
   const int last = max(L - 1, 0);
+  u32x2 qw{0, 0}, kw{0, 0}, vw{0, 0};
+  int32_t id = 0;
+  if constexpr (kAppend) {
+    if (grp == 0) {
+      const int64_t nrow = ((int64_t)s * a.num_kv_heads + kvh) * D + 4 * ti;
+      qw = *(const u32x2*)((const uint16_t*)a.q + orow);
+      kw = *(const u32x2*)((const uint16_t*)a.new_k + nrow);
+      vw = *(const u32x2*)((const uint16_t*)a.new_v + nrow);
+      id = a.block_tables[(int64_t)s * a.max_blocks + (last >> 4)];  // last < 16 * max_blocks
+    }
+  }
   const int64_t Tn = max(T, (int64_t)1);
   const int W = (int)min((int64_t)a.num_workers, Tn);  // as in the decode kernel
   const int w0 = worker_of(c0, Tn, W);
@@ -630,7 +667,7 @@ __global__ __launch_bounds__(256) void decode_merge_wide_kernel(DecodeArgs a) {
   den = 0.f;
   o = f32x4{0.f, 0.f, 0.f, 0.f};
   if (Mt > -INFINITY) {  // else no partial at all
-#pragma unroll
+#pragma unroll 8
     for (int g = 0; g < kG; ++g) {
       const float wgt = fast_exp2(sM[g] - Mt);  // 0 for groups without a partial
       den += wgt * sDen[g];
@@ -658,11 +695,6 @@ __global__ __launch_bounds__(256) void decode_merge_wide_kernel(DecodeArgs a) {
   }
   if constexpr (kAppend) {
     // the newest key as one more partial (m = its score, l = 1, acc = its V row)
-    const int64_t nrow = ((int64_t)s * a.num_kv_heads + kvh) * D + 4 * ti;
-    const u32x2 qw = *(const u32x2*)((const uint16_t*)a.q + orow);
-    const u32x2 kw = *(const u32x2*)((const uint16_t*)a.new_k + nrow);
-    const u32x2 vw = *(const u32x2*)((const uint16_t*)a.new_v + nrow);
-    const int32_t id = a.block_tables[(int64_t)s * a.max_blocks + (last >> 4)];
     float part = 0.f;
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
@@ -899,7 +931,13 @@ void launch_bf16_nw(const DecodeArgs& a, hipStream_t stream) {
 }
 
 template <int D>
-hipError_t launch_decode_d(const DecodeArgs& a, bool bf16, hipStream_t stream) {
+hipError_t launch_decode_d(const DecodeArgs& args, bool bf16, hipStream_t stream) {
+  // More requests than workers, every one needing its own merge only when a cut
+  // between workers falls inside it (no newest token, no prefix partials): the
+  // merge runs over the decode kernel's records of split requests.
+  DecodeArgs a = args;
+  a.merge_splits = a.num_workers > 0 && a.new_k == nullptr && !a.partial_only && a.pre_parts == 0 &&
+                   a.num_seqs > a.num_workers;
   if (bf16) {
     switch (decode_waves(a.num_kv_heads)) {
       case 1: launch_bf16_nw<D, 1>(a, stream); break;
@@ -914,14 +952,14 @@ hipError_t launch_decode_d(const DecodeArgs& a, bool bf16, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 mgrid(a.num_q_heads, a.num_seqs);
-  dim3 hgrid((a.num_q_heads + kMergeHeads - 1) / kMergeHeads, a.num_seqs);
   if (a.num_workers > 0) {
+    dim3 hgrid((a.num_q_heads + kMergeHeads - 1) / kMergeHeads, a.merge_splits ? a.num_workers : a.num_seqs);
     // requests split over more than eight workers on average: the wide merge
     const bool wide = a.num_workers > 8 * a.num_seqs;
     if (wide && a.new_k != nullptr)
-      hipLaunchKernelGGL((decode_merge_wide_kernel<D, true>), mgrid, dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((decode_merge_wide_kernel<D, true>), mgrid, dim3(kWideThreads), 0, stream, a);
     else if (wide)
-      hipLaunchKernelGGL((decode_merge_wide_kernel<D, false>), mgrid, dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((decode_merge_wide_kernel<D, false>), mgrid, dim3(kWideThreads), 0, stream, a);
     else if (a.new_k != nullptr)
       hipLaunchKernelGGL((decode_merge_balanced_kernel<D, true>), hgrid, dim3(64 * kMergeHeads), 0, stream, a);
     else

@@ -146,7 +146,8 @@ DecodeLayout decode_layout(const pa_cache_desc* d, int32_t num_seqs, int32_t max
   l.acc_bytes = align256(rows * d->head_dim * sizeof(float));
   l.ml_bytes = align256(rows * 2 * sizeof(float));
   l.total = l.acc_bytes + l.ml_bytes;
-  if (l.workers > 0) l.total += align256(((size_t)num_seqs + 1) * sizeof(int32_t));
+  // balanced mode: the block prefix sums [S+1], then the split-request records [workers]
+  if (l.workers > 0) l.total += align256(((size_t)num_seqs + 1 + l.workers) * sizeof(int32_t));
   return l;
 }
 
@@ -333,6 +334,7 @@ int decode_impl(const pa_cache_desc* desc, void* out, const void* q, const void*
   a.part_acc = lay.total ? (float*)workspace : nullptr;
   a.part_ml = lay.total ? (float*)((char*)workspace + lay.acc_bytes) : nullptr;
   a.cum_blocks = lay.workers ? (int32_t*)((char*)workspace + lay.acc_bytes + lay.ml_bytes) : nullptr;
+  a.split_req = lay.workers ? a.cum_blocks + num_seqs + 1 : nullptr;
   a.num_blocks = desc->num_blocks;
   a.max_blocks = max_blocks_per_seq;
   a.num_seqs = num_seqs;

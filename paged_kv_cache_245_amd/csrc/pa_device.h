@@ -94,6 +94,10 @@ struct DecodeArgs {
   int32_t num_workers;       // balanced mode: workgroups along the block axis (0 = fixed mode)
   int32_t nontemporal;       // stream K/V past the caches: 1 yes, 0 no, -1 kernel decides
   int32_t* cum_blocks;       // balanced mode: [S+1] prefix sums of blocks per request
+  // balanced mode: [num_workers] the request whose first cut between two workers
+  // falls at the start of this worker's range, or -1 (each split request once)
+  int32_t* split_req;
+  int32_t merge_splits;      // balanced merge grid runs over split_req instead of requests
   float scale_log2;  // scale * log2(e)
   // Append mode (balanced bf16 only; both null otherwise): [S][Hkv][D] K and V of
   // each request's newest token, position context_len - 1. The decode kernel

@@ -252,3 +252,39 @@ def test_batch_size_limit(S):
     w = workloads.custom_decode(S, lens, Hq=8, Hkv=2, D=64, dtype="bf16")
     check(w, 0, f"{S} requests")
     check_append(w, 0, f"append, {S} requests")
+
+
+@pytest.mark.parametrize("workers", [2, 5, 16])
+def test_merge_over_split_requests(workers, monkeypatch):
+    """More requests than workers: the merge visits only the requests a cut between workers
+    falls inside. Long requests span several cuts; many short ones are whole. Plain decode and
+    decode-append (which stores the newest tokens first in this regime) alike."""
+    monkeypatch.setenv("PA_DECODE_WORKERS", str(workers))
+    rng = np.random.default_rng(40 + workers)
+    lens = rng.integers(1, 40, 60)
+    lens[[3, 31, 59]] = [900, 2000, 700]  # each spans several cuts
+    w = workloads.custom_decode(41 + workers, lens.tolist(), Hq=8, Hkv=2, D=128, dtype="bf16")
+    check(w, 0, f"split-request merge, {workers} workers")
+    check_append(w, 0, f"append split-request merge, {workers} workers")
+
+
+def test_merge_over_split_requests_empty_request(monkeypatch):
+    """With the merge over split requests only, a request of length zero (no segment, never
+    merged) still gets its NaN output; its neighbours are unaffected."""
+    monkeypatch.setenv("PA_DECODE_WORKERS", "3")
+    lens = [5, 40, 17, 33, 300, 9, 64, 1]
+    w = workloads.custom_decode(44, lens, Hq=4, Hkv=2, D=64, dtype="bf16")
+    d, k, v = gpu_pools(w)
+    dec = w.decode
+    q = device_tensor(dec.q, "bf16")
+    out = torch.zeros_like(q)
+    bad = dec.context_lens.copy()
+    bad[2] = 0
+    pa.pa_decode(d, out, q, k, v, i32(dec.block_tables), i32(bad), dec.max_context_len, w.scale,
+                 pa.decode_workspace(d, len(lens), dec.max_context_len))
+    torch.cuda.synchronize()
+    o = as64(out)
+    assert np.all(np.isnan(o[2])), "a zero-length request must give NaN"
+    good = [i for i in range(len(lens)) if i != 2]
+    ok, ov = oracle_pools(w)
+    assert_close(o[good], oracle_decode(w, ok, ov)[good], "bf16", "requests next to an empty one")
