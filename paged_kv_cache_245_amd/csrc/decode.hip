@@ -21,7 +21,10 @@
 // merge kernel combines a request's slots: out = sum(2^(m_i-M) acc_i) /
 // sum(2^(m_i-M) l_i), M = max m_i. The slot index is unique because walking the
 // block axis, every segment boundary advances the request, the worker, or both,
-// so (request + worker) strictly increases from segment to segment.
+// so (request + worker) strictly increases from segment to segment. When the
+// requests outnumber the workers, most are whole: each worker then records the
+// request (if any) whose first cut falls at the start of its range, and the
+// merge grid runs over those records instead of over every request.
 // Fixed-partition mode (an explicit partition size, or very large batches):
 // one workgroup per (request, partition of P keys, group of kv heads).
 //
