@@ -288,3 +288,9 @@ def test_merge_over_split_requests_empty_request(monkeypatch):
     good = [i for i in range(len(lens)) if i != 2]
     ok, ov = oracle_pools(w)
     assert_close(o[good], oracle_decode(w, ok, ov)[good], "bf16", "requests next to an empty one")
+    # every request empty: no block at all, every worker idle, every output NaN
+    out.zero_()
+    pa.pa_decode(d, out, q, k, v, i32(dec.block_tables), i32(np.zeros(len(lens))), dec.max_context_len, w.scale,
+                 pa.decode_workspace(d, len(lens), dec.max_context_len))
+    torch.cuda.synchronize()
+    assert np.all(np.isnan(as64(out)))
