@@ -119,3 +119,12 @@ def test_check_mode(monkeypatch):
     assert e.value.status == RANGE
     out = run_shared(w, d, k, v, 4)
     assert np.all(np.isfinite(as64(out)))
+
+
+@pytest.mark.parametrize("seed", [101, 102, 103, 104, 105])
+def test_seed_sweep(seed):
+    """The prefix-shared shape (32/8 heads, D 128, 2,048-token prefix, tails 64-512) with fewer
+    requests, at other seeds: other placements, tails and values."""
+    say(f"  shared-prefix seed {seed}")
+    w = workloads.c3_prefix_shared(seed=seed, num_seqs=24)
+    check(w, w.shared_prefix_tokens // 16, f"shared prefix seed {seed}")

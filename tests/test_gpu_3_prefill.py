@@ -89,3 +89,12 @@ def test_many_requests_heaviest_first_order():
                                  dtype="bf16")
     say(f"  150 requests, {int(new.sum())} rows")
     check(w, "150 requests")
+
+
+@pytest.mark.parametrize("seed", [101, 102, 103, 104, 105])
+def test_seed_sweep(seed):
+    """Mixed-step shape (32/8 heads, D 128, random placement, cached 0-4096) at other seeds,
+    with a chunk length that leaves a ragged last query tile."""
+    say(f"  prefill seed {seed}")
+    w = workloads.c4_mixed_step(seed=seed, num_prefills=3, new_tokens=300, num_decodes=2)
+    check(w, f"prefill seed {seed}")
