@@ -14,7 +14,8 @@ import torch
 
 import paged_kv_cache_245_amd as pa
 import workloads
-from gpu_support import device_tensor, gpu_pools, i32, say
+from gpu_support import as64, assert_close, device_tensor, gpu_pools, i32, say
+from oracle_support import oracle_decode, oracle_pools
 from workloads import f32_to_bf16_bits
 
 pytestmark = pytest.mark.gpu
@@ -91,3 +92,48 @@ def test_step_graph_replays_match_eager():
         assert np.all(np.isfinite(out_g.float().cpu().numpy()))
         outs.append(bits(out_g))
     assert not np.array_equal(outs[0], outs[1])  # the replays did see the new inputs
+
+
+def test_decode_batch_steps_replayed_match_oracle():
+    """The decode batch (64 requests, contexts 512-4096, 32/8 heads, D 128) as bench.py times
+    it: several pa_decode_append calls captured in one HIP graph and replayed. Every replay
+    leaves the pools as pa_write_kv of the newest tokens would, and the output matches the
+    oracle and the eager call bit for bit."""
+    say("  decode batch steps replayed from a graph")
+    w = workloads.make(2)
+    d, k, v = gpu_pools(w, include_step=False)
+    dec, sw = w.decode, w.step_write
+    S = len(dec.context_lens)
+    q = device_tensor(dec.q, "bf16")
+    key, value = device_tensor(sw.key, "bf16"), device_tensor(sw.value, "bf16")
+    tables, lens = i32(dec.block_tables), i32(dec.context_lens)
+    ws = pa.decode_workspace(d, S, dec.max_context_len)
+    out_e, out_g = torch.empty_like(q), torch.empty_like(q)
+
+    def call(out):
+        pa.pa_decode_append(d, out, q, key, value, k, v, tables, lens, dec.max_context_len, w.scale, ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(out_e)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    eager = bits(out_e)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(4):
+            call(out_g)
+    ok, ov = oracle_pools(w)
+    ref = oracle_decode(w, ok, ov)
+    for rep in range(3):
+        out_g.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(out_g), eager), f"replay {rep}: output differs from the eager call"
+        call(out_e)  # eager work between the replays
+        torch.cuda.synchronize()
+    assert np.array_equal(k.view(torch.int16).cpu().numpy().view(np.uint16), ok)
+    assert np.array_equal(v.view(torch.int16).cpu().numpy().view(np.uint16), ov)
+    assert_close(as64(out_g), ref, "bf16", "decode batch, graph-replayed")
