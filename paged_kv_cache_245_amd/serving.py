@@ -4,14 +4,20 @@ A step (arcyou teardown of vLLM paged attention, "Continuous batching: rebuild
 the batch every step") mixes prompt chunks and single generated tokens. Given
 the batch that libpa_host.so's scheduler planned (host.Scheduler.schedule) and
 the block operations the pool queued for it (host.BlockPool.take_ops), this
-module issues, on one stream: the block operations in their order
+module issues, on the caller's stream: the block operations in their order
 (pa_copy_blocks for copy-on-write copies, pa_swap_blocks for swap-outs and
 swap-ins, consecutive operations of one kind batched into one call when none
 writes a block another reads or writes), one copy of the step's metadata to
 the GPU, pa_write_kv for the K/V of the requests given more than one token,
 pa_prefill_chunk for those requests, and pa_decode_append for the ones given
-exactly one (their new K/V is stored by the decode itself). Marshalling and
-sequencing only; the work runs in libpa.so's kernels.
+exactly one (their new K/V is stored by the decode itself). When a step has
+both, the decode runs on a second stream (default priority) forked after the
+write and joined before the step returns: the two calls touch disjoint memory
+(the decode stores only into each one-token request's own last block; blocks
+shared with other requests are full and never written), and the decode's
+workgroups fill the compute units that the prefill's last, lightest work items
+leave idle. Marshalling and sequencing only; the work runs in libpa.so's
+kernels.
 """
 from __future__ import annotations
 
@@ -65,6 +71,7 @@ class StepRunner:
         self.meta = torch.empty(self.n_meta, dtype=torch.int32, device=self.device)
         self.ws = pa.decode_workspace(desc, max_seqs, max_blocks_per_seq * 16, 0, self.device)
         self.ws_bytes = 0 if self.ws is None else self.ws.numel()
+        self.side = torch.cuda.Stream(self.device)  # default priority, like every stream here
 
     def run_ops(self, ops):
         """The pool's block operations (kind, source, destination), in order."""
@@ -115,15 +122,21 @@ class StepRunner:
         tables = self.meta[o_tab:o_slot].view(S, mb)
         slots = self.meta[o_slot:end]
         n_pf = int(batch.query_start_loc[-1])
-        if P:
-            pa.pa_write_kv(self.desc, key[:n_pf], value[:n_pf], self.k, self.v, slots[:n_pf])
-            pa.pa_prefill_chunk(self.desc, out[:n_pf], q[:n_pf], self.k, self.v, qsl, seq[:P], tables[:P],
-                                int(batch.counts[:P].max()), int(batch.seq_lens[:P].max()), self.scale)
         if S > P:
             need = pa.pa_decode_workspace_size(self.desc, S - P, int(batch.seq_lens[P:].max()))
             if need > self.ws_bytes:
                 raise ValueError("decode workspace too small for this step")
+        fork = P > 0 and S > P
+        if P:
+            pa.pa_write_kv(self.desc, key[:n_pf], value[:n_pf], self.k, self.v, slots[:n_pf])
+            if fork:
+                self.side.wait_stream(stream)
+            pa.pa_prefill_chunk(self.desc, out[:n_pf], q[:n_pf], self.k, self.v, qsl, seq[:P], tables[:P],
+                                int(batch.counts[:P].max()), int(batch.seq_lens[:P].max()), self.scale)
+        if S > P:
             # a one-token request's new token is its newest, at position seq_len - 1
             pa.pa_decode_append(self.desc, out[n_pf:N], q[n_pf:N], key[n_pf:N], value[n_pf:N], self.k,
                                 self.v, tables[P:], seq[P:], int(batch.seq_lens[P:].max()), self.scale,
-                                self.ws)
+                                self.ws, stream=self.side if fork else stream)
+            if fork:
+                stream.wait_stream(self.side)

@@ -34,3 +34,48 @@ def test_mixed_step():
     got = as64(out)
     assert_close(got[:T], oracle_prefill(w, ok, ov), "bf16", "step prefill")
     assert_close(got[T:], oracle_decode(w, ok, ov), "bf16", "step decode")
+
+
+def test_mixed_step_two_streams():
+    """The step as the step runner issues it: the prefill rows written, then the chunked
+    prefill on the caller's stream and pa_decode_append (storing the decode tokens) on a
+    second stream forked after the write and joined at the end. Pools and outputs equal
+    those of the same calls on one stream, bit for bit, and match the oracle."""
+    say("  mixed step config 4, decode on a second stream")
+    w = workloads.make(4)
+    st, p, dec = w.step_write, w.prefill, w.decode
+    q_all = device_tensor(w.query, "bf16")
+    T = p.q.shape[0]
+    key, value = device_tensor(st.key, "bf16"), device_tensor(st.value, "bf16")
+    slots = i32(st.slot_mapping)
+    tables = i32(w.block_tables)
+    qsl, seq, lens = i32(p.query_start_loc), i32(p.seq_lens), i32(dec.context_lens)
+    P = w.num_prefills
+
+    def step(k, v, out, ws, side):
+        main = torch.cuda.current_stream()
+        pa.pa_write_kv(d, key[:T], value[:T], k, v, slots[:T])
+        if side is not None:
+            side.wait_stream(main)
+        pa.pa_prefill_chunk(d, out[:T], q_all[:T], k, v, qsl, seq, tables[:P], p.max_query_len,
+                            p.max_seq_len, w.scale)
+        pa.pa_decode_append(d, out[T:], q_all[T:], key[T:], value[T:], k, v, tables[P:], lens,
+                            dec.max_context_len, w.scale, ws, stream=side)
+        if side is not None:
+            main.wait_stream(side)
+
+    d, k1, v1 = gpu_pools(w, include_step=False)
+    k2, v2 = k1.clone(), v1.clone()
+    out1, out2 = torch.empty_like(q_all), torch.empty_like(q_all)
+    ws1 = pa.decode_workspace(d, len(dec.context_lens), dec.max_context_len)
+    ws2 = pa.decode_workspace(d, len(dec.context_lens), dec.max_context_len)
+    step(k1, v1, out1, ws1, None)
+    step(k2, v2, out2, ws2, torch.cuda.Stream())
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(out1), host_bits(out2))
+    assert np.array_equal(host_bits(k1), host_bits(k2)) and np.array_equal(host_bits(v1), host_bits(v2))
+    ok, ov = oracle_pools(w)
+    assert np.array_equal(host_bits(k2), ok) and np.array_equal(host_bits(v2), ov)
+    got = as64(out2)
+    assert_close(got[:T], oracle_prefill(w, ok, ov), "bf16", "two-stream step prefill")
+    assert_close(got[T:], oracle_decode(w, ok, ov), "bf16", "two-stream step decode")
