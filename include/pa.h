@@ -181,6 +181,24 @@ int pa_decode_append(const pa_cache_desc* desc, void* out, const void* q, const 
                      int32_t max_context_len, float scale, int32_t partition_tokens, void* workspace,
                      size_t workspace_bytes, void* stream);
 
+/* pa_decode_append for a decode that runs at the same time as other GPU work,
+ * typically a pa_prefill_chunk of the same scheduler step on another stream
+ * (one step mixes prompt chunks and generated tokens: arcyou teardown, section
+ * "Continuous batching: rebuild the batch every step"). Same arguments, result,
+ * pool update, workspace (pa_decode_workspace_size with partition_tokens 0) and
+ * errors as pa_decode_append with partition_tokens 0. Its kernel keeps each
+ * wavefront within 96 registers and one 16-token block in flight, so that one
+ * wavefront fits on every SIMD beside a running prefill workgroup and the two
+ * calls share the compute units: the decode streams from HBM while the prefill
+ * keeps the matrix cores busy. Run alone it streams more slowly than
+ * pa_decode_append. bf16 pools with at most 8,192 requests; otherwise it is
+ * exactly pa_decode_append. */
+int pa_decode_append_lean(const pa_cache_desc* desc, void* out, const void* q, const void* key,
+                          const void* value, void* k_cache, void* v_cache, const int32_t* block_tables,
+                          int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                          int32_t max_context_len, float scale, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
 /* Decode when every request shares its first prefix_blocks blocks (the same
  * block ids at the start of every row of block_tables, as when a common prompt
  * is found in the prefix cache): the same result as pa_decode. The prefix is

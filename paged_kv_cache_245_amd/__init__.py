@@ -22,6 +22,7 @@ from ._lib import (  # noqa: F401
     pa_copy_blocks,
     pa_decode,
     pa_decode_append,
+    pa_decode_append_lean,
     pa_decode_partition_tokens,
     pa_decode_shared_prefix,
     pa_decode_shared_prefix_workspace_size,

@@ -300,6 +300,140 @@ __device__ __forceinline__ void decode_segment(const DecodeArgs& a, int s, int k
     store_partial<D>(a, pidx_base + (int64_t)h * pidx_stride, acc, m, lsum, g4);
 }
 
+// Lean variant of decode_segment, for a decode that shares compute units with a
+// concurrently running prefill: the prefill's eight wavefronts leave 96 of the
+// 512 registers per SIMD lane, so this wavefront holds one 16-token block of K
+// and V at a time (no second buffer, no block pair). Per block, with lane (n, g4)
+// as in decode_segment:
+//   S^T[16 keys x 16 heads] = K . Q^T    (D/32 MFMA 16x16x32 bf16)
+//   O^T[16 dims x 16 heads] += V^T . P^T (D/16 MFMA 16x16x16 bf16: the lane's own
+//     4 probabilities are its B operand; its A operand is element d of each of
+//     the 4 V rows it loaded, so the output layout is decode_segment's)
+template <int D, bool kNT>
+__device__ __forceinline__ void decode_segment_lean(const DecodeArgs& a, int s, int kvh, int blk_a,
+                                                    int blk_b, int end_tok, bool whole,
+                                                    int64_t pidx_base, int64_t pidx_stride,
+                                                    u32x4* q_lds) {
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  typedef typename VRowT<D>::type VRow;
+  constexpr int kChunks = D / 32;
+  constexpr int kDL = D / 16;
+  // The lane index is made opaque here, so that the per-lane addresses derived from
+  // it are computed per segment instead of being hoisted out of the caller's
+  // segment loop and held (or spilled) across it.
+  int lane = threadIdx.x & 63;
+  asm volatile("" : "+v"(lane));
+  const int n = lane & 15;
+  const int g4 = lane >> 4;
+  const int G = a.group;
+  const int Hkv = a.num_kv_heads;
+  const int h = kvh * G + n;
+  const bool head_ok = n < G;
+  const uint16_t* __restrict__ K = (const uint16_t*)a.k;
+  const uint16_t* __restrict__ V = (const uint16_t*)a.v;
+  const int64_t qo_row = ((int64_t)s * a.num_q_heads + h) * D;
+
+  // The query operands wait in LDS (q_lds: D/32 x 64 slots, each lane its own) and
+  // are read again for every block, instead of D/8 registers held across the loop.
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c)
+    q_lds[c * 64 + lane] = head_ok ? *(const u32x4*)((const uint16_t*)a.q + qo_row + 32 * c + 8 * g4)
+                                   : u32x4{0, 0, 0, 0};
+  f32x4 acc[kDL];
+#pragma unroll
+  for (int t = 0; t < kDL; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, lsum = 0.f;
+  bool poisoned = false;
+
+  const int32_t* table = a.block_tables + (int64_t)s * a.max_blocks;
+  int base = blk_a;
+  int32_t idv = (lane < blk_b - base) ? table[base + lane] : 0;
+  const LaneOffsets o = lane_offsets<D>(kvh, Hkv, n, g4);
+  const int64_t block_bytes = (int64_t)kBlock * o.row_bytes;
+  end_tok = min(end_tok, 16 * blk_b);
+  for (int b = blk_a; b < blk_b; ++b) {
+    if (b - base >= 64) {
+      base += 64;
+      idv = (lane < blk_b - base) ? table[base + lane] : 0;
+    }
+    int32_t id = __builtin_amdgcn_readlane(idv, b - base);
+    if (!block_ok(id, a.num_blocks)) {
+      poisoned = true;
+      id = 0;
+    }
+    const char* kb = (const char*)K + (int64_t)id * block_bytes;
+    const char* vb = (const char*)V + (int64_t)id * block_bytes;
+    u32x4 k[kChunks];
+    VRow v[4];
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) k[c] = load_kv<u32x4, kNT>((const uint16_t*)(kb + o.k + 64 * c));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = load_kv<VRow, kNT>((const uint16_t*)(vb + o.v + j * o.row_bytes));
+
+    // a compiler barrier: the query reads below stay inside the loop (hoisted, they
+    // would hold their registers across it)
+    asm volatile("" ::: "memory");
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+      // one query chunk live at a time (the scheduling barriers keep the next
+      // chunk's read below this product)
+      const u32x4 qc = q_lds[c * 64 + lane];
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k[c]), as_bf16x8(qc), s0, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    float sc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sc[i] = s0[i] * a.scale_log2;
+    const int valid = min(16, end_tok - 16 * b);
+    if (valid < 16) {  // keys past the range: score -inf (by selection), V row 0
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (4 * g4 + j >= valid) {
+          sc[j] = -INFINITY;
+          v[j] = VRow{};
+        }
+      }
+    }
+    float tmax = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    const float m_new = fmaxf(m, tmax);
+    const float alpha = fast_exp2(m - m_new);
+    float p[4];
+    float psum = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      p[j] = fast_exp2(sc[j] - m_new);
+      psum += p[j];
+    }
+    lsum = lsum * alpha + psum;
+    m = m_new;
+    const v4i16 pb = __builtin_bit_cast(v4i16, u32x2{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])});
+#pragma unroll
+    for (int d = 0; d < kDL; ++d) {
+      const int sh = 16 * (d & 1);
+      const uint32_t e0 = (v[0][d >> 1] >> sh) & 0xffffu, e1 = (v[1][d >> 1] >> sh) & 0xffffu;
+      const uint32_t e2 = (v[2][d >> 1] >> sh) & 0xffffu, e3 = (v[3][d >> 1] >> sh) & 0xffffu;
+      const v4i16 va = __builtin_bit_cast(v4i16, u32x2{e0 | (e1 << 16), e2 | (e3 << 16)});
+      acc[d] *= alpha;
+      acc[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, acc[d], 0, 0, 0);
+    }
+    // and the next block's loads stay below this block's products (one block of K
+    // and V live at a time)
+    asm volatile("" ::: "memory");
+  }
+
+  lsum += __shfl_xor(lsum, 16, 64);
+  lsum += __shfl_xor(lsum, 32, 64);
+  if (poisoned) lsum = __builtin_nanf("");
+  if (!head_ok) return;
+  if (whole)
+    store_final<D>((uint16_t*)a.out, qo_row, acc, lsum, g4);
+  else
+    store_partial<D>(a, pidx_base + (int64_t)h * pidx_stride, acc, m, lsum, g4);
+}
+
 // Worker holding global block b when T >= W blocks are split over W workers
 // (worker w owns blocks [w*T/W, (w+1)*T/W), never an empty range).
 __device__ __forceinline__ int worker_of(int64_t b, int64_t T, int W) {
@@ -325,9 +459,11 @@ __device__ __forceinline__ int request_blocks(const DecodeArgs& a, int s) {
 // Balanced mode: grid (W, kv-head groups); dynamic LDS holds S+1 ints.
 // kAppend: the pool is read up to each request's newest token and every segment
 // leaves a partial, which the merge combines with the newest key.
-template <int D, int NW, bool kAppend>
-__global__ __launch_bounds__(64 * NW) void decode_bf16_balanced_kernel(DecodeArgs a) {
+// kLean: one wavefront per workgroup, segments through decode_segment_lean.
+template <int D, int NW, bool kAppend, bool kLean>
+__device__ __forceinline__ void balanced_body(const DecodeArgs& a) {
   extern __shared__ int32_t cum[];
+  __shared__ u32x4 q_lds[kLean ? (D / 32) * 64 : 1];  // the lean segments' query operands
   __shared__ int32_t wave_total[NW];
   constexpr int kThreads = 64 * NW;
   const int tid = threadIdx.x;
@@ -408,14 +544,33 @@ __global__ __launch_bounds__(64 * NW) void decode_bf16_balanced_kernel(DecodeArg
       const bool whole = !kAppend && !a.partial_only && pos == cs && seg_end == ce;
       const int64_t slot = (int64_t)s + w;
       const int b0 = a.skip_blocks + pos - cs, b1 = a.skip_blocks + seg_end - cs;  // table indices
-      if (nt)
-        decode_segment<D, true>(a, s, kvh, b0, b1, n_keys, whole, slot * a.num_q_heads, 1);
-      else
-        decode_segment<D, false>(a, s, kvh, b0, b1, n_keys, whole, slot * a.num_q_heads, 1);
+      if constexpr (kLean) {
+        if (nt)
+          decode_segment_lean<D, true>(a, s, kvh, b0, b1, n_keys, whole, slot * a.num_q_heads, 1, q_lds);
+        else
+          decode_segment_lean<D, false>(a, s, kvh, b0, b1, n_keys, whole, slot * a.num_q_heads, 1, q_lds);
+      } else {
+        if (nt)
+          decode_segment<D, true>(a, s, kvh, b0, b1, n_keys, whole, slot * a.num_q_heads, 1);
+        else
+          decode_segment<D, false>(a, s, kvh, b0, b1, n_keys, whole, slot * a.num_q_heads, 1);
+      }
       pos = seg_end;
     }
     ++s;
   }
+}
+
+template <int D, int NW, bool kAppend>
+__global__ __launch_bounds__(64 * NW) void decode_bf16_balanced_kernel(DecodeArgs a) {
+  balanced_body<D, NW, kAppend, false>(a);
+}
+
+// The lean decode: grid (W, kv heads), one wavefront each, within 96 registers so
+// that one fits on every SIMD beside a running prefill workgroup.
+template <int D, bool kAppend>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(5))) void decode_bf16_lean_kernel(DecodeArgs a) {
+  balanced_body<D, 1, kAppend, true>(a);
 }
 
 // (M, den, o) of one fold combined with another's (M2, den2, o2), each relative
@@ -917,7 +1072,15 @@ void launch_grid(const DecodeArgs& a, hipStream_t stream) {
 
 template <int D, int NW>
 void launch_bf16_nw(const DecodeArgs& a, hipStream_t stream) {
-  if (a.num_workers > 0) {
+  if (a.num_workers > 0 && a.lean) {
+    const size_t lds = sizeof(int32_t) * (size_t)(a.num_seqs + 1);
+    if (a.new_k != nullptr)
+      hipLaunchKernelGGL((decode_bf16_lean_kernel<D, true>), dim3(a.num_workers, a.num_kv_heads), dim3(64),
+                         lds, stream, a);
+    else
+      hipLaunchKernelGGL((decode_bf16_lean_kernel<D, false>), dim3(a.num_workers, a.num_kv_heads), dim3(64),
+                         lds, stream, a);
+  } else if (a.num_workers > 0) {
     const int groups = (a.num_kv_heads + NW - 1) / NW;
     const size_t lds = sizeof(int32_t) * (size_t)(a.num_seqs + 1);
     if (a.new_k != nullptr)

@@ -120,6 +120,14 @@ int32_t balanced_workers(const pa_cache_desc* d) {
   return w > 0 ? w : 1;
 }
 
+// Lean decode: about 1,024 wavefronts, one per SIMD of a 256-CU MI355X, each a
+// kv head of one workgroup.
+int32_t lean_workers(const pa_cache_desc* d) {
+  const int forced = env_int("PA_DECODE_LEAN_WORKERS", 0);  // tuning override
+  if (forced > 0) return forced;
+  return std::max(1, 1024 / d->num_kv_heads);
+}
+
 struct DecodeLayout {
   int32_t partition;  // fixed mode
   int32_t max_parts;  // fixed mode
@@ -271,7 +279,8 @@ int decode_impl(const pa_cache_desc* desc, void* out, const void* q, const void*
                 const void* new_v, const void* k_cache, const void* v_cache,
                 const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
                 int32_t num_seqs, int32_t max_context_len, float scale, int32_t partition_tokens,
-                void* workspace, size_t workspace_bytes, void* stream, int32_t prefix_blocks = 0) {
+                void* workspace, size_t workspace_bytes, void* stream, int32_t prefix_blocks = 0,
+                bool lean = false) {
   int st = validate_desc(desc);
   if (st != PA_OK) return st;
   if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs is negative");
@@ -345,6 +354,12 @@ int decode_impl(const pa_cache_desc* desc, void* out, const void* q, const void*
   a.partition_tokens = lay.partition;
   a.max_parts = lay.max_parts;
   a.num_workers = lay.workers;
+  if (lean && lay.workers > 0 && !prefix) {
+    // one wavefront per workgroup and about four per compute unit (one per SIMD);
+    // never more workers than the workspace was sized for
+    a.lean = 1;
+    a.num_workers = std::max(1, std::min<int32_t>(lay.workers, lean_workers(desc)));
+  }
   a.nontemporal = nontemporal_mode(desc, num_seqs, max_context_len, lay.workers > 0);
   a.scale_log2 = scale * pa::kLog2e;
   if (prefix) {
@@ -381,7 +396,7 @@ int decode_impl(const pa_cache_desc* desc, void* out, const void* q, const void*
     // token in. With more requests than workers most are whole, and writing
     // their output directly (after a small store of the newest tokens) is cheaper
     // than sending every request through the merge.
-    if (lay.workers > 0 && desc->dtype == PA_BF16 && num_seqs <= lay.workers) {
+    if (lay.workers > 0 && desc->dtype == PA_BF16 && num_seqs <= a.num_workers) {
       a.new_k = new_k;  // the merge attends and stores the newest token
       a.new_v = new_v;
     } else {
@@ -436,6 +451,18 @@ int pa_decode_append(const pa_cache_desc* desc, void* out, const void* q, const 
   return decode_impl(desc, out, q, key, value, k_cache, v_cache, block_tables, max_blocks_per_seq,
                      context_lens, num_seqs, max_context_len, scale, partition_tokens, workspace,
                      workspace_bytes, stream);
+}
+
+int pa_decode_append_lean(const pa_cache_desc* desc, void* out, const void* q, const void* key,
+                          const void* value, void* k_cache, void* v_cache, const int32_t* block_tables,
+                          int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                          int32_t max_context_len, float scale, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  if (num_seqs > 0 && (key == nullptr || value == nullptr))
+    return fail(PA_ERR_INVALID_ARG, "null pointer argument");
+  return decode_impl(desc, out, q, key, value, k_cache, v_cache, block_tables, max_blocks_per_seq,
+                     context_lens, num_seqs, max_context_len, scale, 0, workspace, workspace_bytes, stream,
+                     0, true);
 }
 
 int pa_prefill_chunk(const pa_cache_desc* desc, void* out, const void* q, const void* k_cache,

@@ -98,6 +98,7 @@ struct DecodeArgs {
   // falls at the start of this worker's range, or -1 (each split request once)
   int32_t* split_req;
   int32_t merge_splits;      // balanced merge grid runs over split_req instead of requests
+  int32_t lean;              // balanced mode: the lean decode kernel (one wavefront per workgroup)
   float scale_log2;  // scale * log2(e)
   // Append mode (balanced bf16 only; both null otherwise): [S][Hkv][D] K and V of
   // each request's newest token, position context_len - 1. The decode kernel

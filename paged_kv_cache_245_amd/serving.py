@@ -12,11 +12,12 @@ the GPU, pa_write_kv for the K/V of the requests given more than one token,
 pa_prefill_chunk for those requests, and pa_decode_append for the ones given
 exactly one (their new K/V is stored by the decode itself). When a step has
 both, the decode runs on a second stream (default priority) forked after the
-write and joined before the step returns: the two calls touch disjoint memory
-(the decode stores only into each one-token request's own last block; blocks
-shared with other requests are full and never written), and the decode's
-workgroups fill the compute units that the prefill's last, lightest work items
-leave idle. Marshalling and sequencing only; the work runs in libpa.so's
+write and joined before the step returns, through pa_decode_append_lean, whose
+wavefronts fit beside the prefill's on every compute unit: the prefill keeps
+the matrix cores busy while the decode streams K/V from HBM. The two calls
+touch disjoint memory (the decode stores only into each one-token request's
+own last block; blocks shared with other requests are full and never
+written). Marshalling and sequencing only; the work runs in libpa.so's
 kernels.
 """
 from __future__ import annotations
@@ -135,8 +136,10 @@ class StepRunner:
                                 int(batch.counts[:P].max()), int(batch.seq_lens[:P].max()), self.scale)
         if S > P:
             # a one-token request's new token is its newest, at position seq_len - 1
-            pa.pa_decode_append(self.desc, out[n_pf:N], q[n_pf:N], key[n_pf:N], value[n_pf:N], self.k,
-                                self.v, tables[P:], seq[P:], int(batch.seq_lens[P:].max()), self.scale,
-                                self.ws, stream=self.side if fork else stream)
+            args = (self.desc, out[n_pf:N], q[n_pf:N], key[n_pf:N], value[n_pf:N], self.k, self.v,
+                    tables[P:], seq[P:], int(batch.seq_lens[P:].max()), self.scale, self.ws)
             if fork:
+                pa.pa_decode_append_lean(*args, stream=self.side)
                 stream.wait_stream(self.side)
+            else:
+                pa.pa_decode_append(*args, stream=stream)

@@ -294,3 +294,77 @@ def test_merge_over_split_requests_empty_request(monkeypatch):
                  pa.decode_workspace(d, len(lens), dec.max_context_len))
     torch.cuda.synchronize()
     assert np.all(np.isnan(as64(out)))
+
+
+def run_append_lean(w, d, k, v):
+    """pa_decode_append_lean with the step's new tokens (one per decode request)."""
+    dec, sw = w.decode, w.step_write
+    S = len(dec.context_lens)
+    q = device_tensor(dec.q, w.spec.dtype)
+    out = torch.empty_like(q)
+    ws = pa.decode_workspace(d, S, dec.max_context_len, 0)
+    pa.pa_decode_append_lean(d, out, q, device_tensor(sw.key, w.spec.dtype), device_tensor(sw.value, w.spec.dtype),
+                             k, v, i32(dec.block_tables), i32(dec.context_lens), dec.max_context_len, w.scale, ws)
+    torch.cuda.synchronize()
+    return out
+
+
+def check_lean(w, what):
+    """The lean decode leaves the pools as pa_write_kv would and matches the oracle."""
+    d, k, v = gpu_pools(w, include_step=False)
+    out = run_append_lean(w, d, k, v)
+    ok, ov = oracle_pools(w)
+    assert np.array_equal(host_bits(k), ok) and np.array_equal(host_bits(v), ov)
+    assert_close(as64(out), oracle_decode(w, ok, ov), w.spec.dtype, what)
+    return out
+
+
+@pytest.mark.parametrize("index", [2, 3])
+def test_lean_configs(index):
+    say(f"  lean decode config {index}")
+    check_lean(workloads.make(index), f"lean config {index}")
+
+
+@pytest.mark.parametrize("group,D", [(g, D) for g in (1, 2, 4, 8, 16) for D in (64, 128)])
+def test_lean_shapes(group, D):
+    w = workloads.custom_decode(500 + group + D, [1, 15, 16, 17, 31, 33, 300, 1111], Hq=2 * group,
+                                Hkv=2, D=D, dtype="bf16")
+    out = check_lean(w, f"lean G={group} D={D}")
+    # a context of one token returns that token's V exactly
+    assert np.array_equal(host_bits(out)[0], np.repeat(w.step_write.value[0], group, axis=0))
+
+
+@pytest.mark.parametrize("workers", [1, 3, 16, 100000])
+def test_lean_worker_counts(workers, monkeypatch):
+    """Any number of lean workers, down to one block each and fewer than the requests (the
+    newest tokens are then stored first and the merge runs over split requests)."""
+    monkeypatch.setenv("PA_DECODE_LEAN_WORKERS", str(workers))
+    rng = np.random.default_rng(60 + workers)
+    lens = rng.integers(1, 600, 40)
+    w = workloads.custom_decode(61 + workers, lens.tolist(), Hq=8, Hkv=2, D=128, dtype="bf16")
+    check_lean(w, f"lean workers {workers}")
+
+
+def test_lean_bad_length_and_block():
+    """As pa_decode_append: a zero length and an out-of-range id give that request NaN, and
+    nothing is stored for it; the other requests are unaffected."""
+    w = workloads.custom_decode(13, [5, 40, 17, 33], Hq=4, Hkv=2, D=64, dtype="bf16")
+    d, k, v = gpu_pools(w, include_step=False)
+    dec, sw = w.decode, w.step_write
+    lens = dec.context_lens.copy()
+    lens[1] = 0
+    tables = dec.block_tables.copy()
+    tables[3, 2] = w.spec.num_blocks + 7
+    q = device_tensor(dec.q, "bf16")
+    out = torch.zeros_like(q)
+    ws = pa.decode_workspace(d, 4, dec.max_context_len, 0)
+    pa.pa_decode_append_lean(d, out, q, device_tensor(sw.key, "bf16"), device_tensor(sw.value, "bf16"), k, v,
+                             i32(tables), i32(lens), dec.max_context_len, w.scale, ws)
+    torch.cuda.synchronize()
+    o = as64(out)
+    assert np.all(np.isnan(o[[1, 3]])), "bad requests must give NaN"
+    ok, ov = oracle_pools(w, include_step=False)
+    good = [0, 2]
+    oracle.write_kv(ok, ov, sw.key[good], sw.value[good], sw.slot_mapping[good])
+    assert np.array_equal(host_bits(k), ok) and np.array_equal(host_bits(v), ov)
+    assert_close(o[good], oracle_decode(w, ok, ov)[good], "bf16", "lean, requests next to bad ones")

@@ -94,3 +94,25 @@ def test_prefill_occupancy(remarks):
         seen += 1
         assert r["Occupancy"] >= 2, (name, r)
     assert seen >= 20  # {64, 128} x {1, 2, 4, 8, 16} x {causal, shared prefix}
+
+
+def test_lean_decode_fits_beside_prefill(remarks):
+    """The lean decode kernel exists to share compute units with a running prefill
+    workgroup (eight wavefronts, two per SIMD): one lean wavefront per SIMD must fit in
+    the 512 registers per SIMD lane that two prefill wavefronts leave."""
+    def regs(r):
+        return -(-(r["VGPRs"] + r.get("AGPRs", 0)) // 8) * 8  # allocation granule of 8
+    prefill = {}
+    for name, r in remarks["prefill.hip"].items():
+        m = re.search(r"prefill_bf16_kernelILi(\d+)E", name)
+        if m:
+            prefill[int(m.group(1))] = max(prefill.get(int(m.group(1)), 0), regs(r))
+    seen = 0
+    for name, r in remarks["decode.hip"].items():
+        m = re.search(r"decode_bf16_lean_kernelILi(\d+)E", name)
+        if not m:
+            continue
+        seen += 1
+        D = int(m.group(1))
+        assert regs(r) + 2 * prefill[D] <= 512, (name, r, prefill[D])
+    assert seen == 4  # D in {64, 128} x {append, plain}
