@@ -314,7 +314,8 @@ def check_lean(w, what):
     d, k, v = gpu_pools(w, include_step=False)
     out = run_append_lean(w, d, k, v)
     ok, ov = oracle_pools(w)
-    assert np.array_equal(host_bits(k), ok) and np.array_equal(host_bits(v), ov)
+    view = (lambda a: a.view(np.uint32)) if w.spec.dtype == "f32" else (lambda a: a)  # NaN-poisoned slots
+    assert np.array_equal(view(host_bits(k)), view(ok)) and np.array_equal(view(host_bits(v)), view(ov))
     assert_close(as64(out), oracle_decode(w, ok, ov), w.spec.dtype, what)
     return out
 
@@ -368,3 +369,11 @@ def test_lean_bad_length_and_block():
     oracle.write_kv(ok, ov, sw.key[good], sw.value[good], sw.slot_mapping[good])
     assert np.array_equal(host_bits(k), ok) and np.array_equal(host_bits(v), ov)
     assert_close(o[good], oracle_decode(w, ok, ov)[good], "bf16", "lean, requests next to bad ones")
+
+
+@pytest.mark.parametrize("dtype,Hq,Hkv,D", [("f32", 8, 2, 64), ("bf16", 32, 16, 128), ("bf16", 4, 4, 64)])
+def test_lean_other_layouts(dtype, Hq, Hkv, D):
+    """fp32 pools (the lean call is then exactly pa_decode_append), sixteen kv heads (fewer
+    lean workers than kv-head groups' workers), and as many kv heads as q heads."""
+    w = workloads.custom_decode(70 + Hkv + D, [1, 16, 17, 250, 700, 1300], Hq=Hq, Hkv=Hkv, D=D, dtype=dtype)
+    check_lean(w, f"lean {dtype} Hq={Hq} Hkv={Hkv} D={D}")
