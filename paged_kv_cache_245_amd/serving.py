@@ -58,8 +58,12 @@ class StepRunner:
     """
 
     def __init__(self, desc, k_cache, v_cache, scale, max_seqs, max_tokens, max_blocks_per_seq,
-                 device="cuda", host_k=None, host_v=None):
-        """host_k/host_v: the pinned CPU swap space [num_host_blocks, 16, Hkv, D], if any."""
+                 device="cuda", host_k=None, host_v=None, side_stream=None):
+        """host_k/host_v: the pinned CPU swap space [num_host_blocks, 16, Hkv, D], if any.
+        side_stream: the stream for the decode beside the prefill (default: a new one). The
+        two overlap only if HIP put this stream on another hardware queue than the caller's;
+        it hands out GPU_MAX_HW_QUEUES (4 by default) queues to streams, so a stream
+        created early in the process, among the first few, normally has its own."""
         self.desc, self.k, self.v, self.scale = desc, k_cache, v_cache, float(scale)
         self.host_k, self.host_v = host_k, host_v
         self.max_seqs, self.max_tokens, self.max_blocks = max_seqs, max_tokens, max_blocks_per_seq
@@ -72,7 +76,8 @@ class StepRunner:
         self.meta = torch.empty(self.n_meta, dtype=torch.int32, device=self.device)
         self.ws = pa.decode_workspace(desc, max_seqs, max_blocks_per_seq * 16, 0, self.device)
         self.ws_bytes = 0 if self.ws is None else self.ws.numel()
-        self.side = torch.cuda.Stream(self.device)  # default priority, like every stream here
+        # default priority, like every stream here
+        self.side = side_stream if side_stream is not None else torch.cuda.Stream(self.device)
 
     def run_ops(self, ops):
         """The pool's block operations (kind, source, destination), in order."""

@@ -137,3 +137,43 @@ def test_decode_batch_steps_replayed_match_oracle():
     assert np.array_equal(k.view(torch.int16).cpu().numpy().view(np.uint16), ok)
     assert np.array_equal(v.view(torch.int16).cpu().numpy().view(np.uint16), ov)
     assert_close(as64(out_g), ref, "bf16", "decode batch, graph-replayed")
+
+
+def test_shared_prefix_call_replayed_matches_eager():
+    """pa_decode_shared_prefix (prefix pass, tails' decode, merge) captured in a HIP graph
+    and replayed gives the eager call's output bit for bit, replay after replay."""
+    say("  shared-prefix call replayed from a graph")
+    w = workloads.c3_prefix_shared(seed=31, num_seqs=40)
+    d, k, v = gpu_pools(w)
+    dec = w.decode
+    S = len(dec.context_lens)
+    pb = w.shared_prefix_tokens // 16
+    q = device_tensor(dec.q, "bf16")
+    tables, lens = i32(dec.block_tables), i32(dec.context_lens)
+    n = pa.pa_decode_shared_prefix_workspace_size(d, S, dec.max_context_len, pb)
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    out_e, out_g = torch.empty_like(q), torch.empty_like(q)
+
+    def call(out):
+        pa.pa_decode_shared_prefix(d, out, q, k, v, tables, lens, dec.max_context_len, pb, w.scale, ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(out_e)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    eager = bits(out_e)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(out_g)
+    for rep in range(3):
+        out_g.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(out_g), eager), f"replay {rep}"
+        call(out_e)  # eager work between the replays
+        torch.cuda.synchronize()
+    ok, ov = oracle_pools(w)
+    assert_close(as64(out_g), oracle_decode(w, ok, ov), "bf16", "shared prefix, graph-replayed")
