@@ -102,7 +102,9 @@ int32_t pa_decode_partition_tokens(const pa_cache_desc* desc, int32_t num_seqs,
 
 /* Bytes of device workspace pa_decode needs for these sizes and this partition
  * size (0 = automatic). 0 means no workspace is needed. Returns 0 for invalid
- * arguments as well; pa_decode reports those. */
+ * arguments as well; pa_decode reports those. The balanced split's worker
+ * count follows the compute units of the calling thread's current device, so
+ * the size is for that device: call it with the device of the decode current. */
 size_t pa_decode_workspace_size(const pa_cache_desc* desc, int32_t num_seqs,
                                 int32_t max_context_len, int32_t partition_tokens);
 
@@ -161,8 +163,9 @@ int pa_prefill_chunk(const pa_cache_desc* desc, void* out, const void* q,
 /* Decode after appending each request's newest token: the same result as
  * pa_write_kv of those tokens into their slots followed by pa_decode. Where the
  * decode runs in its balanced bf16 mode (the default for bf16 pools,
- * partition_tokens == 0) and the requests do not outnumber its workgroups (256
- * with 8 kv heads), no write launch is added: the decode reads the pool up to
+ * partition_tokens == 0) and the requests do not outnumber its workgroups
+ * (eight wavefronts per compute unit of the device: 256 workgroups with 8 kv
+ * heads on a 256-CU MI355X), no write launch is added: the decode reads the pool up to
  * each newest token, and its merge pass attends that token and stores it.
  * Otherwise the tokens are stored first by a small kernel, then the decode runs. The newest token of
  * request s sits at position context_lens[s] - 1 (context_lens counts it); its

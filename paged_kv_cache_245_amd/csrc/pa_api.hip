@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdlib>
 #include <string>
@@ -109,23 +110,45 @@ int env_int(const char* name, int dflt) {
   return e != nullptr ? std::atoi(e) : dflt;
 }
 
-// Balanced decode: enough workgroups for ~2048 wavefronts (8 per compute unit on
-// a 256-CU MI355X), each wavefront one kv head of one workgroup.
+// Compute units of the calling thread's current device, read once per device
+// (256 on MI355X). The decode's worker counts derive from it; a device the
+// runtime cannot name is taken to have 256.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cus[kMaxDevices];
+
+int device_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  int n = g_cus[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+    (void)hipGetLastError();
+    n = 256;
+  }
+  g_cus[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+// Balanced decode: enough workgroups for eight wavefronts per compute unit
+// (2,048 on a 256-CU MI355X), each wavefront one kv head of one workgroup.
 int32_t balanced_workers(const pa_cache_desc* d) {
-  const int forced = env_int("PA_DECODE_WORKERS", 0);
+  const int forced = env_int("PA_DECODE_WORKERS", 0);  // tuning override
   if (forced > 0) return forced;
   const int nw = pa::decode_waves(d->num_kv_heads);
   const int groups = (d->num_kv_heads + nw - 1) / nw;
-  const int w = 2048 / (nw * groups);
+  const int w = 8 * device_cus() / (nw * groups);
   return w > 0 ? w : 1;
 }
 
-// Lean decode: about 1,024 wavefronts, one per SIMD of a 256-CU MI355X, each a
-// kv head of one workgroup.
+// Lean decode: one wavefront per SIMD (four per compute unit; 1,024 on a 256-CU
+// MI355X), each a kv head of one workgroup.
 int32_t lean_workers(const pa_cache_desc* d) {
   const int forced = env_int("PA_DECODE_LEAN_WORKERS", 0);  // tuning override
   if (forced > 0) return forced;
-  return std::max(1, 1024 / d->num_kv_heads);
+  return std::max(1, 4 * device_cus() / d->num_kv_heads);
 }
 
 struct DecodeLayout {
