@@ -30,18 +30,57 @@ def test_config_full(index):
     check(workloads.make(index))
 
 
-def test_long_context_sampled():
-    """131072-token contexts: sampled (request, head) outputs against the oracle, all finite."""
-    say("  decode config 5 (long context)")
+@pytest.fixture(scope="module")
+def long_context():
+    """The long-context workload (8 requests x 131,072 tokens, 64 q / 8 kv heads) once per
+    module: the workload, the oracle's pools after the step's write, and the oracle's output
+    for every one of the 8 x 64 (request, q head) rows."""
+    say("  long-context workload and its oracle (all 512 rows)")
     w = workloads.make(5)
-    d, k, v = gpu_pools(w)
-    out = as64(run_decode(w, d, k, v))
-    assert np.all(np.isfinite(out))
     ok, ov = oracle_pools(w)
-    pairs = [(s, h) for s in range(8) for h in (s, 31, 63 - s)]
-    ref = oracle_decode(w, ok, ov, pairs=pairs)
-    idx = tuple(np.array(pairs).T)
-    assert_close(out[idx], ref[idx], "bf16", "config 5 sampled")
+    ref = oracle_decode(w, ok, ov)
+    assert np.all(np.isfinite(ref))
+    return w, ok, ov, ref
+
+
+def same_pools(k, v, ok, ov):
+    """GPU pools equal the oracle's bit for bit, every slot included."""
+    assert np.array_equal(host_bits(k), ok), "K pool differs from the oracle's"
+    assert np.array_equal(host_bits(v), ov), "V pool differs from the oracle's"
+
+
+@pytest.mark.timeout(600)
+def test_long_context_decode_all_rows(long_context):
+    """pa_decode over 131,072-token contexts: every (request, q head) row against the oracle."""
+    w, ok, ov, ref = long_context
+    say("  decode config 5 (long context), all rows")
+    d, k, v = gpu_pools(w)
+    same_pools(k, v, ok, ov)
+    assert_close(as64(run_decode(w, d, k, v)), ref, "bf16", "config 5, pa_decode, all 512 rows")
+
+
+@pytest.mark.timeout(600)
+def test_long_context_append_all_rows(long_context):
+    """pa_decode_append at the long-context shape (requests split over every worker, so the
+    wide merge attends and stores the newest tokens): pools bit-exact afterwards, every row
+    against the oracle."""
+    w, ok, ov, ref = long_context
+    say("  decode_append config 5 (long context), all rows")
+    d, k, v = gpu_pools(w, include_step=False)
+    out = run_append(w, d, k, v)
+    same_pools(k, v, ok, ov)
+    assert_close(as64(out), ref, "bf16", "config 5, pa_decode_append, all 512 rows")
+
+
+@pytest.mark.timeout(600)
+def test_long_context_append_lean_all_rows(long_context):
+    """pa_decode_append_lean at the long-context shape, as for pa_decode_append."""
+    w, ok, ov, ref = long_context
+    say("  decode_append_lean config 5 (long context), all rows")
+    d, k, v = gpu_pools(w, include_step=False)
+    out = run_append_lean(w, d, k, v)
+    same_pools(k, v, ok, ov)
+    assert_close(as64(out), ref, "bf16", "config 5, pa_decode_append_lean, all 512 rows")
 
 
 @pytest.mark.parametrize("part", [0, 4096, 512, 256, 48, 16])
