@@ -202,6 +202,28 @@ int pa_decode_append_lean(const pa_cache_desc* desc, void* out, const void* q, c
                           int32_t max_context_len, float scale, void* workspace, size_t workspace_bytes,
                           void* stream);
 
+/* pa_decode_append for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc. The
+ * same arguments, result, pool update and errors as pa_decode_append, without
+ * the workspace: the split-KV partials go to one fixed device array of
+ * PA_NOALLOC_SCRATCH_BYTES bytes that the library holds on every GPU it runs
+ * on until the process ends. The call allocates nothing (no hipMalloc, no
+ * hipFree, no allocating library routine); the first call on a device looks up
+ * that device's copy of the array once. Sizes whose workspace
+ * (pa_decode_workspace_size) exceeds PA_NOALLOC_SCRATCH_BYTES are refused with
+ * PA_ERR_WORKSPACE before anything is enqueued; 64 MiB holds, with 32 q heads
+ * and head_dim 128 on a 256-CU device, the balanced split of up to 3,776
+ * requests of any length. Every call on one GPU shares that GPU's array, and
+ * the array keeps the last call's contents (nothing in it needs clearing):
+ * calls that overlap on one GPU, e.g. on two streams, race on it and give
+ * wrong results. Check mode (PA_CHECK=1) synchronises and copies metadata to
+ * the host as for pa_decode_append; leave it off where those are not allowed. */
+#define PA_NOALLOC_SCRATCH_BYTES (64u << 20)
+int pa_decode_append_noalloc(const pa_cache_desc* desc, void* out, const void* q, const void* key,
+                             const void* value, void* k_cache, void* v_cache, const int32_t* block_tables,
+                             int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                             int32_t max_context_len, float scale, int32_t partition_tokens, void* stream);
+
 /* Decode when every request shares its first prefix_blocks blocks (the same
  * block ids at the start of every row of block_tables, as when a common prompt
  * is found in the prefix cache): the same result as pa_decode. The prefix is

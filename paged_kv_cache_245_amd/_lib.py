@@ -20,7 +20,8 @@ PA_BF16 = 1
 BLOCK_SIZE = 16
 
 EXPORTED = ("pa_write_kv", "pa_decode_partition_tokens", "pa_decode_workspace_size", "pa_decode",
-            "pa_decode_append", "pa_decode_append_lean", "pa_decode_shared_prefix_workspace_size", "pa_decode_shared_prefix",
+            "pa_decode_append", "pa_decode_append_lean", "pa_decode_append_noalloc",
+            "pa_decode_shared_prefix_workspace_size", "pa_decode_shared_prefix",
             "pa_prefill_chunk", "pa_copy_blocks", "pa_swap_blocks", "pa_gather_kv", "pa_strerror", "pa_last_error_detail",
             "pa_version", "pa_bench_copy", "pa_bench_read", "pa_bench_flush")
 
@@ -70,6 +71,7 @@ def load():
         "pa_decode": (ctypes.c_int, [D, P, P, P, P, P, I32, P, I32, I32, F, I32, P, SZ, P]),
         "pa_decode_append": (ctypes.c_int, [D, P, P, P, P, P, P, P, I32, P, I32, I32, F, I32, P, SZ, P]),
         "pa_decode_append_lean": (ctypes.c_int, [D, P, P, P, P, P, P, P, I32, P, I32, I32, F, P, SZ, P]),
+        "pa_decode_append_noalloc": (ctypes.c_int, [D, P, P, P, P, P, P, P, I32, P, I32, I32, F, I32, P]),
         "pa_decode_shared_prefix_workspace_size": (SZ, [D, I32, I32, I32]),
         "pa_decode_shared_prefix": (ctypes.c_int, [D, P, P, P, P, P, I32, P, I32, I32, I32, F, P, SZ, P]),
         "pa_prefill_chunk": (ctypes.c_int, [D, P, P, P, P, P, P, P, I32, I32, I32, I32, I32, F, P]),
@@ -260,6 +262,33 @@ def pa_decode_append_lean(desc, out, q, key, value, k_cache, v_cache, block_tabl
                                       _ptr(context_lens), S, int(max_context_len), float(scale),
                                       _ptr(workspace), ws_bytes, _stream(stream, q))
     _check(st, "pa_decode_append_lean")
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # PA_NOALLOC_SCRATCH_BYTES
+
+
+def pa_decode_append_noalloc(desc, out, q, key, value, k_cache, v_cache, block_tables, context_lens,
+                             max_context_len, scale, partition_tokens=0, stream=None):
+    """pa_decode_append without a workspace argument: the library's fixed per-GPU scratch
+    array holds the split-KV partials (for callers that cannot allocate device memory)."""
+    dt = torch_dtype(desc)
+    for t, n in ((out, "out"), (q, "q"), (key, "key"), (value, "value"), (k_cache, "k_cache"),
+                 (v_cache, "v_cache")):
+        _need(t, dt, n)
+    _need(block_tables, torch.int32, "block_tables", 2)
+    _need(context_lens, torch.int32, "context_lens", 1)
+    S = context_lens.numel()
+    _pools(desc, k_cache, v_cache)
+    _rows(q, "q", S, desc.num_q_heads, desc.head_dim)
+    _rows(out, "out", S, desc.num_q_heads, desc.head_dim)
+    _rows(key, "key", S, desc.num_kv_heads, desc.head_dim)
+    _rows(value, "value", S, desc.num_kv_heads, desc.head_dim)
+    _table_rows(block_tables, S)
+    st = load().pa_decode_append_noalloc(ctypes.byref(desc), _ptr(out), _ptr(q), _ptr(key), _ptr(value),
+                                         _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), block_tables.shape[1],
+                                         _ptr(context_lens), S, int(max_context_len), float(scale),
+                                         int(partition_tokens), _stream(stream, q))
+    _check(st, "pa_decode_append_noalloc")
 
 
 def pa_decode_shared_prefix_workspace_size(desc, num_seqs, max_context_len, prefix_blocks) -> int:

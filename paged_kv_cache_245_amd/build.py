@@ -24,7 +24,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpa.so")
 
 SOURCES = ["pa_api.hip", "write_kv.hip", "decode.hip", "prefill.hip", "copy_blocks.hip",
-           "gather_kv.hip", "bench_kernels.hip"]
+           "gather_kv.hip", "bench_kernels.hip", "noalloc.hip"]
 HOST_SOURCES = ["block_pool.cpp", "sched.cpp"]
 HOST_LIB = os.path.join(PKG, "libpa_host.so")
 ARCH = "gfx950"

@@ -230,6 +230,10 @@ int32_t nontemporal_mode(const pa_cache_desc* d, int32_t num_seqs, int32_t max_c
 
 }  // namespace
 
+namespace pa {
+int set_error_detail(int status, const char* what) { return fail(status, what); }
+}  // namespace pa
+
 extern "C" {
 
 int pa_version(void) { return PA_VERSION; }

@@ -146,6 +146,10 @@ struct PrefillArgs {
   float* part_ml;   // [num_seqs][Hq][key_splits][2]
 };
 
+// Records `what` as the detail of the calling thread's last error (returned by
+// pa_last_error_detail) and returns `status`.
+int set_error_detail(int status, const char* what);
+
 hipError_t launch_write_kv(const void* key, const void* value, void* k_cache, void* v_cache,
                            const int32_t* slots, int64_t num_tokens, int row_bytes,
                            int64_t num_slots, hipStream_t stream);
