@@ -160,6 +160,32 @@ int pa_prefill_chunk(const pa_cache_desc* desc, void* out, const void* q,
                      int32_t max_blocks_per_seq, int32_t num_seqs, int32_t num_tokens,
                      int32_t max_query_len, int32_t max_seq_len, float scale, void* stream);
 
+/* Chunked prefill after storing each chunk's new K/V: the same result and pool
+ * update as pa_write_kv of every chunk token's K/V into its slot (row i of
+ * request s's chunk sits at position seq_lens[s] - n_s + i, in block
+ * block_tables[s][position / 16] at offset position % 16) followed by
+ * pa_prefill_chunk, in one launch and without the separate write: the kernel
+ * reads the chunk's own keys and values from key/value (the cached ones from
+ * the pool) and stores the new rows into the pool. With pa_decode_append, a
+ * step that mixes prompt chunks and generated tokens (arcyou teardown, section
+ * "Continuous batching: rebuild the batch every step") then needs no write
+ * launch at all; the KV cache grows one token at a time and every token
+ * re-reads all past K/V (arcyou teardown, "The problem both ideas solve").
+ * Reading the chunk's rows from key/value is slower than reading them from the
+ * pool, so on MI355X this call takes about as long as pa_write_kv followed by
+ * pa_prefill_chunk; it saves the launch, not time.
+ *   key, value   [num_tokens][Hkv][D] bf16, row t the new token of query row t
+ * The blocks covering each chunk's positions must be in its table, distinct
+ * between requests and not read by any other request of the call (shared
+ * blocks are copied on write first); check mode verifies that the chunks'
+ * slots are distinct. All other arguments and the errors are those of
+ * pa_prefill_chunk. PA_BF16 only. */
+int pa_prefill_chunk_append(const pa_cache_desc* desc, void* out, const void* q, const void* key,
+                            const void* value, void* k_cache, void* v_cache, const int32_t* query_start_loc,
+                            const int32_t* seq_lens, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            int32_t num_seqs, int32_t num_tokens, int32_t max_query_len, int32_t max_seq_len,
+                            float scale, void* stream);
+
 /* Decode after appending each request's newest token: the same result as
  * pa_write_kv of those tokens into their slots followed by pa_decode. Where the
  * decode runs in its balanced bf16 mode (the default for bf16 pools,

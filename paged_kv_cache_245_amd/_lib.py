@@ -22,7 +22,7 @@ BLOCK_SIZE = 16
 EXPORTED = ("pa_write_kv", "pa_decode_partition_tokens", "pa_decode_workspace_size", "pa_decode",
             "pa_decode_append", "pa_decode_append_lean", "pa_decode_append_noalloc",
             "pa_decode_shared_prefix_workspace_size", "pa_decode_shared_prefix",
-            "pa_prefill_chunk", "pa_copy_blocks", "pa_swap_blocks", "pa_gather_kv", "pa_strerror", "pa_last_error_detail",
+            "pa_prefill_chunk", "pa_prefill_chunk_append", "pa_copy_blocks", "pa_swap_blocks", "pa_gather_kv", "pa_strerror", "pa_last_error_detail",
             "pa_version", "pa_bench_copy", "pa_bench_read", "pa_bench_flush")
 
 
@@ -75,6 +75,7 @@ def load():
         "pa_decode_shared_prefix_workspace_size": (SZ, [D, I32, I32, I32]),
         "pa_decode_shared_prefix": (ctypes.c_int, [D, P, P, P, P, P, I32, P, I32, I32, I32, F, P, SZ, P]),
         "pa_prefill_chunk": (ctypes.c_int, [D, P, P, P, P, P, P, P, I32, I32, I32, I32, I32, F, P]),
+        "pa_prefill_chunk_append": (ctypes.c_int, [D, P, P, P, P, P, P, P, P, P, I32, I32, I32, I32, I32, F, P]),
         "pa_copy_blocks": (ctypes.c_int, [D, P, P, P, I64, P]),
         "pa_swap_blocks": (ctypes.c_int, [D, P, P, P, P, I64, P, I64, I32, P]),
         "pa_gather_kv": (ctypes.c_int, [D, P, P, P, P, P, I32, P, I32, I32, P]),
@@ -339,6 +340,32 @@ def pa_prefill_chunk(desc, out, q, k_cache, v_cache, query_start_loc, seq_lens, 
                                  int(max_query_len), int(max_seq_len), float(scale),
                                  _stream(stream, q))
     _check(st, "pa_prefill_chunk")
+
+
+def pa_prefill_chunk_append(desc, out, q, key, value, k_cache, v_cache, query_start_loc, seq_lens,
+                            block_tables, max_query_len, max_seq_len, scale, stream=None):
+    """pa_prefill_chunk after storing the chunks' new K/V (key/value [T, Hkv, D], row t the
+    new token of query row t) into their slots, in one launch."""
+    dt = torch_dtype(desc)
+    for t, n in ((out, "out"), (q, "q"), (key, "key"), (value, "value"), (k_cache, "k_cache"),
+                 (v_cache, "v_cache")):
+        _need(t, dt, n)
+    for t, n in ((query_start_loc, "query_start_loc"), (seq_lens, "seq_lens")):
+        _need(t, torch.int32, n, 1)
+    _need(block_tables, torch.int32, "block_tables", 2)
+    S = seq_lens.numel()
+    _pools(desc, k_cache, v_cache)
+    _rows(q, "q", 0, desc.num_q_heads, desc.head_dim)
+    _rows(out, "out", q.shape[0], desc.num_q_heads, desc.head_dim)
+    _rows(key, "key", q.shape[0], desc.num_kv_heads, desc.head_dim)
+    _rows(value, "value", q.shape[0], desc.num_kv_heads, desc.head_dim)
+    _shape(query_start_loc, "query_start_loc", S + 1)
+    _table_rows(block_tables, S)
+    st = load().pa_prefill_chunk_append(ctypes.byref(desc), _ptr(out), _ptr(q), _ptr(key), _ptr(value),
+                                        _ptr(k_cache), _ptr(v_cache), _ptr(query_start_loc), _ptr(seq_lens),
+                                        _ptr(block_tables), block_tables.shape[1], S, q.shape[0],
+                                        int(max_query_len), int(max_seq_len), float(scale), _stream(stream, q))
+    _check(st, "pa_prefill_chunk_append")
 
 
 def pa_copy_blocks(desc, k_cache, v_cache, block_pairs, stream=None):

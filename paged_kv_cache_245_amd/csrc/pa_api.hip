@@ -492,11 +492,13 @@ int pa_decode_append_lean(const pa_cache_desc* desc, void* out, const void* q, c
                      0, true);
 }
 
-int pa_prefill_chunk(const pa_cache_desc* desc, void* out, const void* q, const void* k_cache,
-                     const void* v_cache, const int32_t* query_start_loc, const int32_t* seq_lens,
-                     const int32_t* block_tables, int32_t max_blocks_per_seq, int32_t num_seqs,
-                     int32_t num_tokens, int32_t max_query_len, int32_t max_seq_len, float scale,
-                     void* stream) {
+namespace {
+// pa_prefill_chunk; pa_prefill_chunk_append when new_k/new_v are given.
+int prefill_impl(const pa_cache_desc* desc, void* out, const void* q, const void* new_k, const void* new_v,
+                 const void* k_cache, const void* v_cache, const int32_t* query_start_loc,
+                 const int32_t* seq_lens, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                 int32_t num_seqs, int32_t num_tokens, int32_t max_query_len, int32_t max_seq_len,
+                 float scale, void* stream) {
   int st = validate_desc(desc);
   if (st != PA_OK) return st;
   if (desc->dtype != PA_BF16) return fail(PA_ERR_UNSUPPORTED, "prefill supports bf16 only");
@@ -532,6 +534,18 @@ int pa_prefill_chunk(const pa_cache_desc* desc, void* out, const void* q, const 
     }
     st = check_tables(tables, max_blocks_per_seq, lens, desc->num_blocks);
     if (st != PA_OK) return st;
+    if (new_k != nullptr) {  // the chunks' new tokens go to distinct slots
+      std::unordered_set<int64_t> seen;
+      for (int s = 0; s < num_seqs; ++s)
+        for (int i = 0; i < qsl[s + 1] - qsl[s]; ++i) {
+          const int pos = lens[s] - (qsl[s + 1] - qsl[s]) + i;
+          const int64_t slot = (int64_t)tables[(size_t)s * max_blocks_per_seq + pos / PA_BLOCK_SIZE] *
+                                   PA_BLOCK_SIZE + pos % PA_BLOCK_SIZE;
+          if (!seen.insert(slot).second)
+            return fail(PA_ERR_RANGE, "slot " + std::to_string(slot) + " of request " + std::to_string(s) +
+                                          " is written twice");
+        }
+    }
   }
   pa::PrefillArgs a{};
   a.q = (const uint16_t*)q;
@@ -550,9 +564,33 @@ int pa_prefill_chunk(const pa_cache_desc* desc, void* out, const void* q, const 
   a.num_q_heads = desc->num_q_heads;
   a.num_kv_heads = desc->num_kv_heads;
   a.scale_log2 = scale * pa::kLog2e;
+  a.new_k = (const uint16_t*)new_k;
+  a.new_v = (const uint16_t*)new_v;
   return hip_status(pa::launch_prefill(a, desc->head_dim, desc->num_q_heads / desc->num_kv_heads,
                                        as_stream(stream)),
                     "prefill launch");
+}
+}  // namespace
+
+int pa_prefill_chunk(const pa_cache_desc* desc, void* out, const void* q, const void* k_cache,
+                     const void* v_cache, const int32_t* query_start_loc, const int32_t* seq_lens,
+                     const int32_t* block_tables, int32_t max_blocks_per_seq, int32_t num_seqs,
+                     int32_t num_tokens, int32_t max_query_len, int32_t max_seq_len, float scale,
+                     void* stream) {
+  return prefill_impl(desc, out, q, nullptr, nullptr, k_cache, v_cache, query_start_loc, seq_lens,
+                      block_tables, max_blocks_per_seq, num_seqs, num_tokens, max_query_len, max_seq_len,
+                      scale, stream);
+}
+
+int pa_prefill_chunk_append(const pa_cache_desc* desc, void* out, const void* q, const void* key,
+                            const void* value, void* k_cache, void* v_cache, const int32_t* query_start_loc,
+                            const int32_t* seq_lens, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            int32_t num_seqs, int32_t num_tokens, int32_t max_query_len, int32_t max_seq_len,
+                            float scale, void* stream) {
+  if (num_seqs > 0 && num_tokens > 0 && (key == nullptr || value == nullptr))
+    return fail(PA_ERR_INVALID_ARG, "null pointer argument");
+  return prefill_impl(desc, out, q, key, value, k_cache, v_cache, query_start_loc, seq_lens, block_tables,
+                      max_blocks_per_seq, num_seqs, num_tokens, max_query_len, max_seq_len, scale, stream);
 }
 
 int pa_copy_blocks(const pa_cache_desc* desc, void* k_cache, void* v_cache,

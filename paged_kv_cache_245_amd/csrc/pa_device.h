@@ -144,6 +144,12 @@ struct PrefillArgs {
   int32_t key_splits;
   float* part_acc;  // [num_seqs][Hq][key_splits][D]
   float* part_ml;   // [num_seqs][Hq][key_splits][2]
+  // Append mode (launch_prefill with both set): [num_tokens][Hkv][D] K and V of
+  // the chunks' own tokens, row t for query row t. The kernel reads a chunk's keys
+  // from here instead of the pool, and each workgroup stores the rows of its own
+  // query positions into the pool (k, v) through the block table.
+  const uint16_t* new_k;
+  const uint16_t* new_v;
 };
 
 // Records `what` as the detail of the calling thread's last error (returned by

@@ -39,6 +39,13 @@
 // their probabilities are exactly zero.
 // The tile loop is unrolled by two, so the LDS stage of every operand read is an
 // immediate offset.
+// Append mode (pa_prefill_chunk_append): the chunk's own keys and values are
+// staged from the caller's new K/V rows instead of the pool (a block that holds
+// both cached and new tokens is read in two masked passes), and each workgroup
+// stores the new rows of its own query positions and kv head into the pool
+// through the block table. No workgroup reads a new token's slot, so the stores
+// need no ordering against the reads; the rows are loaded before the first
+// tiles and stored after the first barrier.
 // Work items (request, kv head, query tile) run heaviest first: workgroup i of
 // the dispatch order takes the item of rank i by cost (see item_of_rank).
 // Within one cost level consecutive workgroups take the kv heads of one
@@ -181,9 +188,10 @@ __device__ void item_of_rank(const PrefillArgs& a, int64_t rank, int kPos, int l
   }
 }
 
-template <int D, int G, bool kCross>
+template <int D, int G, bool kCross, bool kAppend>
 __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a) {
   static_assert(D == 64 || D == 128, "head_dim");
+  static_assert(!(kCross && kAppend), "append mode is for causal chunks");
   constexpr int kPos = kRows / G;            // query positions per workgroup
   constexpr int kCh = D / 8;                 // 16-byte chunks per key row
   constexpr int kTileCh = kBN * kCh;         // chunks per staged tile of K (or V)
@@ -301,15 +309,67 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
     if (!block_ok(id, a.num_blocks)) { poisoned = true; id = 0; }
     const uint16_t* src = (s_is_v ? a.v : a.k) + (int64_t)id * block_elems;
     u32x4* dst = s_is_v ? &Vs[buf][0] : &Ks[buf][0];
-    const bool full = key0 + 16 * (sblk + 1) <= L;  // uniform: the whole block is in range
+    const int kb = key0 + 16 * sblk;  // first key of this wavefront's block
+    const bool full = kb + 16 <= L;   // uniform: the whole block is in range
+    // append mode: keys >= cached are the chunk's own, in the input rows
+    // q0 + key - cached (the same [Hkv][D] layout as a pool row)
+    // (the base of those rows is formed only for lanes that read them)
+    const bool has_new = kAppend && kb + 16 > cached;  // uniform
+    const uint16_t* nbase = nullptr;
+    if constexpr (kAppend) nbase = (s_is_v ? a.new_v : a.new_k) + (int64_t)(q0 + kb - cached) * row_elems;
 #pragma unroll
     for (int i = 0; i < kInstr; ++i) {
+      // row of the tile, and key of the block (kb + (row & 15) = kb + 64 i / kCh + lane / kCh)
       const int row = ((sblk * kInstr + i) * 64 + lane) / kCh;
-      if (full || key0 + row < L)  // past the context: not loaded
-        __builtin_amdgcn_global_load_lds((const void*)(src + src_off[i]),
-                                         (lds_void*)&dst[(sblk * kInstr + i) * 64], 16, 0, 0);
+      const bool in_range = full || key0 + row < L;  // past the context: not loaded
+      lds_void* to = (lds_void*)&dst[(sblk * kInstr + i) * 64];
+      if (!has_new) {
+        if (in_range) __builtin_amdgcn_global_load_lds((const void*)(src + src_off[i]), to, 16, 0, 0);
+      } else {
+        // a block holding both cached and new tokens is read in two masked passes
+        const bool from_new = (lane / kCh) >= cached - kb - (64 * i) / kCh;
+        if (in_range && !from_new) __builtin_amdgcn_global_load_lds((const void*)(src + src_off[i]), to, 16, 0, 0);
+        if (in_range && from_new) __builtin_amdgcn_global_load_lds((const void*)(nbase + src_off[i]), to, 16, 0, 0);
+      }
     }
   };
+
+  // Append mode: this workgroup's share of the chunk's new rows (positions pos0 ..
+  // pos0 + kPos - 1, kv head kvh, K then V), 16 bytes a piece, kStore pieces per
+  // thread and round. The first round is loaded here and stored after the first
+  // barrier; further rounds (G <= 2) are copied there in turn.
+  constexpr int kPieces = kAppend ? 2 * kPos * kCh : 0;
+  constexpr int kStore = 4;
+  u32x4 cp[kStore];
+  int64_t cp_dst[kStore];  // 2 x (16-byte piece index in the pool tensor) + tensor, or -1
+  auto copy_load = [&](int round) {
+#pragma unroll
+    for (int j = 0; j < kStore; ++j) {
+      const int piece = (round * kStore + j) * kThreads + tid;
+      const int v = piece >= kPos * kCh;  // 0: K, 1: V
+      const int rem = piece - v * kPos * kCh;
+      const int p = pos0 + rem / kCh, ch = rem % kCh;
+      cp_dst[j] = -1;
+      if (piece < kPieces && p < nq && cached + p < L) {
+        int32_t id = table[(cached + p) >> 4];
+        if (block_ok(id, a.num_blocks)) {
+          const int64_t row = kv_row(id, (cached + p) & 15, kvh, Hkv, D) + 8 * ch;
+          const uint16_t* srcp = (v ? a.new_v : a.new_k) + ((int64_t)(q0 + p) * Hkv + kvh) * D + 8 * ch;
+          cp[j] = *(const u32x4*)srcp;
+          cp_dst[j] = (row >> 3) * 2 + v;
+        }
+      }
+    }
+  };
+  auto copy_store = [&]() {
+#pragma unroll
+    for (int j = 0; j < kStore; ++j) {
+      if (cp_dst[j] < 0) continue;
+      uint16_t* pool = const_cast<uint16_t*>((cp_dst[j] & 1) ? a.v : a.k);
+      *(u32x4*)(pool + (cp_dst[j] >> 1) * 8) = cp[j];
+    }
+  };
+  if constexpr (kAppend) copy_load(0);
 
   // Per-lane LDS byte addresses of the MFMA operands in stage 0 (stage 1 is +kTileCh*16).
   //   K (A of S^T): row 32 kb + col, logical chunk 2c + half  -> one per c, kb by offset
@@ -349,6 +409,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
   // their loads) and are visible to every wavefront
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  if constexpr (kAppend) {
+    copy_store();
+#pragma unroll 1
+    for (int round = 1; round * kStore * kThreads < kPieces; ++round) {
+      copy_load(round);
+      copy_store();
+    }
+  }
 
   // one tile; the LDS stage is a compile-time constant so that operand
   // addresses take it as an immediate offset
@@ -508,10 +576,13 @@ hipError_t launch_dg(const PrefillArgs& a, hipStream_t stream) {
   if constexpr (kCross) {
     // (query tile, kv head) pairs along x, key ranges along y
     dim3 grid(a.num_kv_heads * ((a.num_seqs + kPos - 1) / kPos), a.key_splits);
-    hipLaunchKernelGGL((prefill_bf16_kernel<D, G, true>), grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, G, true, false>), grid, dim3(kThreads), 0, stream, a);
   } else {
     dim3 grid(a.num_seqs * a.num_kv_heads, (a.max_query_len + kPos - 1) / kPos);
-    hipLaunchKernelGGL((prefill_bf16_kernel<D, G, false>), grid, dim3(kThreads), 0, stream, a);
+    if (a.new_k != nullptr)
+      hipLaunchKernelGGL((prefill_bf16_kernel<D, G, false, true>), grid, dim3(kThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((prefill_bf16_kernel<D, G, false, false>), grid, dim3(kThreads), 0, stream, a);
   }
   return hipGetLastError();
 }

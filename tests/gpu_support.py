@@ -96,6 +96,21 @@ def run_prefill(w, d, k, v, device="cuda"):
     return out
 
 
+def run_prefill_append(w, d, k, v, device="cuda"):
+    """pa_prefill_chunk_append with the chunks' new K/V (the first rows of the step's write,
+    one per query row, in order); stores them into the pools."""
+    p, st = w.prefill, w.step_write
+    T = p.q.shape[0]
+    q_t = device_tensor(p.q, w.spec.dtype, device)
+    out = torch.empty_like(q_t)
+    pa.pa_prefill_chunk_append(d, out, q_t, device_tensor(st.key[:T], w.spec.dtype, device),
+                               device_tensor(st.value[:T], w.spec.dtype, device), k, v,
+                               i32(p.query_start_loc, device), i32(p.seq_lens, device),
+                               i32(p.block_tables, device), p.max_query_len, p.max_seq_len, w.scale)
+    torch.cuda.synchronize()
+    return out
+
+
 def assert_close(got, ref, dtype, what=""):
     """got (GPU output as float64 numpy) vs the oracle's float64 result."""
     mx, rel = TOL[dtype]

@@ -5,8 +5,9 @@ import torch
 
 import paged_kv_cache_245_amd as pa
 import workloads
-from gpu_support import (as64, assert_close, desc_of, device_tensor, gpu_pools, i32, run_decode,
-                         run_prefill, say)
+import oracle
+from gpu_support import (as64, assert_close, desc_of, device_tensor, gpu_pools, host_bits, i32, run_decode,
+                         run_prefill, run_prefill_append, say)
 from oracle_support import oracle_pools, oracle_prefill
 
 pytestmark = pytest.mark.gpu
@@ -98,3 +99,86 @@ def test_seed_sweep(seed):
     say(f"  prefill seed {seed}")
     w = workloads.c4_mixed_step(seed=seed, num_prefills=3, new_tokens=300, num_decodes=2)
     check(w, f"prefill seed {seed}")
+
+
+# ---- pa_prefill_chunk_append: the chunks' K/V read from the input and stored by the call
+
+def oracle_pools_prefill_rows(w):
+    """Oracle pools after set-up and the step's prefill rows only (no decode tokens)."""
+    ok, ov = oracle_pools(w, include_step=False)
+    st, T = w.step_write, w.prefill.q.shape[0]
+    oracle.write_kv(ok, ov, st.key[:T], st.value[:T], st.slot_mapping[:T])
+    return ok, ov
+
+
+def check_append(w, what):
+    """The fused call leaves the pools exactly as pa_write_kv of the chunks' rows would, gives
+    bit for bit the output of pa_write_kv + pa_prefill_chunk, and matches the oracle."""
+    d, k, v = gpu_pools(w, include_step=False)
+    out = run_prefill_append(w, d, k, v)
+    ok, ov = oracle_pools_prefill_rows(w)
+    assert np.array_equal(host_bits(k), ok) and np.array_equal(host_bits(v), ov), f"{what}: pools differ"
+    d2, k2, v2 = gpu_pools(w)  # the step written first (decode tokens too), then the plain call
+    ref_bits = host_bits(run_prefill(w, d2, k2, v2))
+    assert np.array_equal(host_bits(out), ref_bits), f"{what}: differs from write + prefill"
+    assert_close(as64(out), oracle_prefill(w, ok, ov), "bf16", what)
+    return out
+
+
+def test_append_mixed_step_prefill_full():
+    say("  prefill_append config 4")
+    check_append(workloads.make(4), "config 4 prefill, fused append")
+
+
+def test_append_cached_edge_counts():
+    """Chunks starting at the pool's first slot, one token in, inside a block and at 4096."""
+    w = workloads.c4_mixed_step(seed=4, cached=[0, 1, 2047, 4096], num_decodes=2)
+    check_append(w, "fused append, cached {0,1,2047,4096}")
+
+
+@pytest.mark.parametrize("group,D", [(g, D) for g in (1, 2, 4, 8, 16) for D in (64, 128)])
+def test_append_shapes(group, D):
+    """Every GQA group and head dim; cached counts that put the chunk's first token inside
+    a block (5, 100), at a block start (16) and at the first slot (0)."""
+    w = workloads.custom_prefill(400 + group + D, cached=[0, 5, 16, 100], new=[1, 70, 33, 129],
+                                 Hq=2 * group, Hkv=2, D=D, dtype="bf16")
+    check_append(w, f"fused append G={group} D={D}")
+
+
+def test_append_many_requests():
+    """150 chunks of mixed sizes and offsets (the heaviest-first order over many requests)."""
+    rng = np.random.default_rng(82)
+    new = rng.integers(1, 41, 150)
+    cached = rng.integers(0, 301, 150)
+    w = workloads.custom_prefill(82, cached=cached.tolist(), new=new.tolist(), Hq=8, Hkv=2, D=128,
+                                 dtype="bf16")
+    check_append(w, "fused append, 150 requests")
+
+
+def test_append_bad_block():
+    """An out-of-range id for a block that holds new tokens: nothing is stored into it, the
+    request's rows are NaN (its one query tile reads the block), and the other request is
+    unaffected."""
+    say("  prefill_append with a bad block id")
+    w = workloads.custom_prefill(83, cached=[20, 40], new=[30, 50], Hq=8, Hkv=2, D=128, dtype="bf16")
+    d, k, v = gpu_pools(w, include_step=False)
+    p, st = w.prefill, w.step_write
+    T = p.q.shape[0]
+    tables = p.block_tables.copy()
+    tables[1, 4] = w.spec.num_blocks + 3  # positions 64..79 of request 1 (new tokens 64..89)
+    q = device_tensor(p.q, "bf16")
+    out = torch.empty_like(q)
+    pa.pa_prefill_chunk_append(d, out, q, device_tensor(st.key[:T], "bf16"), device_tensor(st.value[:T], "bf16"),
+                               k, v, i32(p.query_start_loc), i32(p.seq_lens), i32(tables), p.max_query_len,
+                               p.max_seq_len, w.scale)
+    torch.cuda.synchronize()
+    o = as64(out)
+    rows1 = np.arange(p.query_start_loc[1], p.query_start_loc[2])
+    assert np.all(np.isnan(o[rows1])), "rows of the request with the bad block must be NaN"
+    ok, ov = oracle_pools(w, include_step=False)
+    keep = np.array([not (s // 16 == int(p.block_tables[1, 4])) for s in st.slot_mapping[:T]])
+    oracle.write_kv(ok, ov, st.key[:T][keep], st.value[:T][keep], st.slot_mapping[:T][keep])
+    assert np.array_equal(host_bits(k), ok) and np.array_equal(host_bits(v), ov)
+    ref = oracle_prefill(w, *oracle_pools_prefill_rows(w))
+    good = np.arange(p.query_start_loc[1])
+    assert_close(o[good], ref[good], "bf16", "fused append, request next to a bad block")

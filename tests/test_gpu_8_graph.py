@@ -1,7 +1,8 @@
 """A whole continuous-batching step captured once in a HIP graph and replayed.
 
 The step is pa_write_kv of the prefill rows, pa_prefill_chunk, and
-pa_decode_append for the one-token requests. No call of the step allocates,
+pa_decode_append for the one-token requests; or, fused, pa_prefill_chunk_append
+(which stores the prefill rows itself) and pa_decode_append. No call of the step allocates,
 clears memory or synchronizes (outside PA_CHECK mode), so the step can be
 captured. Each replay runs with new q/K/V copied into the captured buffers,
 and its output and pools must equal, bit for bit, those of the same calls
@@ -25,8 +26,9 @@ def bits(t):
     return t.view(torch.int16).cpu().numpy()
 
 
-def test_step_graph_replays_match_eager():
-    say("  graph capture of a mixed step")
+@pytest.mark.parametrize("fused", [False, True])
+def test_step_graph_replays_match_eager(fused):
+    say(f"  graph capture of a mixed step (fused prefill: {fused})")
     w = workloads.custom_prefill(21, cached=[0, 40, 100], new=[30, 17, 64], Hq=8, Hkv=2, D=128,
                                  dtype="bf16", decode_lengths=[1, 16, 17, 200, 513])
     d, k0, v0 = gpu_pools(w, include_step=False)
@@ -44,9 +46,13 @@ def test_step_graph_replays_match_eager():
     scale = w.scale
 
     def step(k, v, out):
-        pa.pa_write_kv(d, key[:T], value[:T], k, v, slots)
-        pa.pa_prefill_chunk(d, out[:T], q[:T], k, v, qsl, seq, tables[:P], p.max_query_len, p.max_seq_len,
-                            scale)
+        if fused:
+            pa.pa_prefill_chunk_append(d, out[:T], q[:T], key[:T], value[:T], k, v, qsl, seq, tables[:P],
+                                       p.max_query_len, p.max_seq_len, scale)
+        else:
+            pa.pa_write_kv(d, key[:T], value[:T], k, v, slots)
+            pa.pa_prefill_chunk(d, out[:T], q[:T], k, v, qsl, seq, tables[:P], p.max_query_len,
+                                p.max_seq_len, scale)
         pa.pa_decode_append(d, out[T:], q[T:], key[T:], value[T:], k, v, tables[P:], lens,
                             dec.max_context_len, scale, ws)
 

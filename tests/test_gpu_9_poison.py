@@ -15,7 +15,8 @@ import torch
 
 import paged_kv_cache_245_amd as pa
 import workloads
-from gpu_support import desc_of, device_tensor, gpu_pools, host_bits, i32, run_decode, run_prefill, say, write
+from gpu_support import (desc_of, device_tensor, gpu_pools, host_bits, i32, run_decode, run_prefill,
+                         run_prefill_append, say, write)
 
 pytestmark = pytest.mark.gpu
 
@@ -83,6 +84,18 @@ def test_prefill(D):
     d, kp, vp = gpu_pools(w)
     _, kz, vz = zero_pools(w)
     same_bits(run_prefill(w, d, kp, vp), run_prefill(w, d, kz, vz), "prefill")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_prefill_append(D):
+    """The fused call reads the chunks' own keys from the input and the cached ones from the
+    pool, through blocks that hold both."""
+    say(f"  poison vs zeros: prefill_append D={D}")
+    w = workloads.custom_prefill(95 + D, cached=[0, 5, 63, 64, 100, 1000], new=[1, 16, 3, 70, 37, 200],
+                                 Hq=8, Hkv=2, D=D, dtype="bf16")
+    d, kp, vp = gpu_pools(w, include_step=False)
+    _, kz, vz = zero_pools(w, include_step=False)
+    same_bits(run_prefill_append(w, d, kp, vp), run_prefill_append(w, d, kz, vz), "prefill_append")
 
 
 def test_decode_shared_prefix():
