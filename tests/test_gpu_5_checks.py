@@ -134,3 +134,36 @@ def test_check_mode_decode_append(monkeypatch):
                         w.scale, ws)
     torch.cuda.synchronize()
     assert np.all(np.isfinite(as64(out)))
+
+
+def test_check_mode_prefill_append(monkeypatch):
+    """Check mode validates pa_prefill_chunk_append's metadata like pa_prefill_chunk's, and
+    also refuses two chunk tokens mapped to one slot (two requests whose tables name the same
+    block for new tokens), before any launch; the pools stay untouched."""
+    w = workloads.custom_prefill(87, cached=[3, 9], new=[20, 5], Hq=4, Hkv=2, D=64, dtype="bf16")
+    d, k, v = gpu_pools(w, include_step=False)
+    monkeypatch.setenv("PA_CHECK", "1")
+    p, st = w.prefill, w.step_write
+    T = p.q.shape[0]
+    q = device_tensor(p.q, "bf16")
+    key, val = device_tensor(st.key[:T], "bf16"), device_tensor(st.value[:T], "bf16")
+    out = torch.empty_like(q)
+    before = host_bits(k).copy()
+    tables = p.block_tables.copy()
+    tables[1, 0] = tables[0, 0]  # request 1's new tokens (positions 9..13) on request 0's (positions 3..15)
+    with pytest.raises(pa.PAError) as e:
+        pa.pa_prefill_chunk_append(d, out, q, key, val, k, v, i32(p.query_start_loc), i32(p.seq_lens),
+                                   i32(tables), p.max_query_len, p.max_seq_len, w.scale)
+    assert e.value.status == RANGE and "written twice" in pa.pa_last_error_detail()
+    bad = p.block_tables.copy()
+    bad[0, 1] = w.spec.num_blocks
+    with pytest.raises(pa.PAError) as e:
+        pa.pa_prefill_chunk_append(d, out, q, key, val, k, v, i32(p.query_start_loc), i32(p.seq_lens),
+                                   i32(bad), p.max_query_len, p.max_seq_len, w.scale)
+    assert e.value.status == RANGE
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(k), before)  # nothing was launched
+    pa.pa_prefill_chunk_append(d, out, q, key, val, k, v, i32(p.query_start_loc), i32(p.seq_lens),
+                               i32(p.block_tables), p.max_query_len, p.max_seq_len, w.scale)
+    torch.cuda.synchronize()
+    assert np.all(np.isfinite(as64(out)))
