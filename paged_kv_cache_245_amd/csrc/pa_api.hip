@@ -185,8 +185,9 @@ DecodeLayout decode_layout(const pa_cache_desc* d, int32_t num_seqs, int32_t max
 // Shared-prefix decode: the balanced decode's workspace (for the tails), then the
 // prefix pass's partials [S][Hq][splits][D] and [S][Hq][splits][2]. The prefix
 // keys are split into ranges of whole 64-key tiles so that the prefix pass has
-// about 256 workgroups (256 packed rows of one kv head each; one per compute
-// unit): more, shorter ones paid their set-up twice and left more partials.
+// about one workgroup (256 packed rows of one kv head) per two compute units:
+// that timed as one per compute unit did and leaves half the partials, which
+// the merge reads back; more, shorter ranges paid their set-up twice.
 struct PrefixLayout {
   DecodeLayout dec;
   int32_t key_chunk;
@@ -203,7 +204,7 @@ PrefixLayout prefix_layout(const pa_cache_desc* d, int32_t num_seqs, int32_t max
   const int group = d->num_q_heads / d->num_kv_heads;
   const int64_t row_tiles = ((int64_t)num_seqs * group + 255) / 256;
   const int64_t wgs = (int64_t)d->num_kv_heads * row_tiles;
-  const int64_t target = std::max(1, env_int("PA_PREFIX_WORKGROUPS", 256));  // tuning override
+  const int64_t target = std::max(1, env_int("PA_PREFIX_WORKGROUPS", device_cus() / 2));  // tuning override
   int64_t splits = std::min<int64_t>(std::max<int64_t>(tiles, 1), std::max<int64_t>(1, (target + wgs - 1) / wgs));
   const int64_t tiles_per = (tiles + splits - 1) / splits;
   p.key_chunk = (int32_t)(64 * std::max<int64_t>(tiles_per, 1));
