@@ -70,6 +70,21 @@ def test_long_context_append_all_rows(long_context):
     out = run_append(w, d, k, v)
     same_pools(k, v, ok, ov)
     assert_close(as64(out), ref, "bf16", "config 5, pa_decode_append, all 512 rows")
+    # the benchmark's step: the same call launched back to back on the same pools (each
+    # call stores the same newest rows again); every result equals the first, bit for bit
+    dec, sw = w.decode, w.step_write
+    q = device_tensor(dec.q, "bf16")
+    key, val = device_tensor(sw.key, "bf16"), device_tensor(sw.value, "bf16")
+    tables, lens = i32(dec.block_tables), i32(dec.context_lens)
+    ws = pa.decode_workspace(d, len(dec.context_lens), dec.max_context_len)
+    outs = [torch.empty_like(q) for _ in range(4)]
+    for o in outs:
+        pa.pa_decode_append(d, o, q, key, val, k, v, tables, lens, dec.max_context_len, w.scale, ws)
+    torch.cuda.synchronize()
+    first = host_bits(out)
+    for o in outs:
+        assert np.array_equal(host_bits(o), first), "back-to-back calls differ"
+    same_pools(k, v, ok, ov)
 
 
 @pytest.mark.timeout(600)
