@@ -330,10 +330,17 @@ int pa_version(void);
  * pa_bench_read  reads `bytes` (a multiple of 16) from src and writes one word
  *                per workgroup into sink (>= 4096 floats): the read ceiling.
  * pa_bench_flush overwrites `bytes` (a multiple of 16) of buf, e.g. to evict
- *                the last-level cache between timed runs. */
+ *                the last-level cache between timed runs.
+ * pa_bench_mfma  `workgroups` workgroups of 512 threads run `iters` rounds of 8
+ *                MFMA 32x32x16 bf16 products each (8 * 32768 flop per wavefront and
+ *                round) on operand fragments read once from `operands` (device,
+ *                at least workgroups * 512 * 128 bytes of bf16 values); each thread
+ *                writes one float to sink (workgroups * 512 floats): the dense
+ *                matrix-core rate the chip sustains on that data. */
 int pa_bench_copy(void* dst, const void* src, size_t bytes, void* stream);
 int pa_bench_read(const void* src, size_t bytes, float* sink, void* stream);
 int pa_bench_flush(void* buf, size_t bytes, void* stream);
+int pa_bench_mfma(const void* operands, int32_t workgroups, int32_t iters, float* sink, void* stream);
 
 #ifdef __cplusplus
 }

@@ -23,7 +23,7 @@ EXPORTED = ("pa_write_kv", "pa_decode_partition_tokens", "pa_decode_workspace_si
             "pa_decode_append", "pa_decode_append_lean", "pa_decode_append_noalloc",
             "pa_decode_shared_prefix_workspace_size", "pa_decode_shared_prefix",
             "pa_prefill_chunk", "pa_prefill_chunk_append", "pa_copy_blocks", "pa_swap_blocks", "pa_gather_kv", "pa_strerror", "pa_last_error_detail",
-            "pa_version", "pa_bench_copy", "pa_bench_read", "pa_bench_flush")
+            "pa_version", "pa_bench_copy", "pa_bench_read", "pa_bench_flush", "pa_bench_mfma")
 
 
 class PAError(RuntimeError):
@@ -85,6 +85,7 @@ def load():
         "pa_bench_copy": (ctypes.c_int, [P, P, SZ, P]),
         "pa_bench_read": (ctypes.c_int, [P, SZ, P, P]),
         "pa_bench_flush": (ctypes.c_int, [P, SZ, P]),
+        "pa_bench_mfma": (ctypes.c_int, [P, I32, I32, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -442,3 +443,11 @@ def pa_bench_flush(buf, nbytes, stream=None):
     if nbytes > _nbytes(buf):
         raise ValueError("nbytes exceeds buf")
     _check(load().pa_bench_flush(_ptr(buf), nbytes, _stream(stream, buf)), "pa_bench_flush")
+
+
+def pa_bench_mfma(operands, workgroups, iters, sink, stream=None):
+    """operands: bf16 values, at least workgroups * 512 * 64 of them; sink: workgroups * 512 floats."""
+    if _nbytes(operands) < workgroups * 512 * 128 or _nbytes(sink) < workgroups * 512 * 4:
+        raise ValueError("operands or sink too small for this many workgroups")
+    _check(load().pa_bench_mfma(_ptr(operands), int(workgroups), int(iters), _ptr(sink),
+                                _stream(stream, operands)), "pa_bench_mfma")

@@ -1,7 +1,8 @@
 // bench_kernels.hip - measurement kernels: a plain 16-byte-per-lane copy (known
 // traffic, used to calibrate hardware byte counters), a streaming read (the
-// achievable HBM read ceiling), and a buffer overwrite that evicts the
-// last-level cache between timed runs.
+// achievable HBM read ceiling), a buffer overwrite that evicts the last-level
+// cache between timed runs, and a dense bf16 MFMA loop on caller-supplied
+// operands (the matrix-core rate the chip sustains on such data).
 #include "pa_device.h"
 
 namespace pa {
@@ -60,7 +61,41 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(u32x4* __restrict__ buf
   }
 }
 
+// MFMA 32x32x16 bf16 on every SIMD: 8 wavefronts per workgroup, each lane holding
+// 8 operand fragments of 16 bytes read once from `operands` (fragment i of thread
+// t of workgroup b at [(b * 512 + t) * 8 + i]), then `iters` rounds of 8 products
+// into 4 independent accumulators; each thread writes one checksum float.
+__global__ __launch_bounds__(512) void mfma_kernel(const u32x4* __restrict__ operands, int iters,
+                                                   float* __restrict__ sink) {
+  const int64_t t = (int64_t)blockIdx.x * 512 + threadIdx.x;
+  bf16x8 fa[4], fb[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    fa[i] = as_bf16x8(operands[t * 8 + i]);
+    fb[i] = as_bf16x8(operands[t * 8 + 4 + i]);
+  }
+  f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[(2 * j) & 3], fb[(2 * j + 1) & 3], c0, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[(2 * j + 1) & 3], fb[(2 * j + 2) & 3], c1, 0, 0, 0);
+      c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[(2 * j + 2) & 3], fb[(2 * j + 3) & 3], c2, 0, 0, 0);
+      c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[(2 * j + 3) & 3], fb[(2 * j) & 3], c3, 0, 0, 0);
+    }
+  }
+  float x = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) x += c0[i] + c1[i] + c2[i] + c3[i];
+  sink[t] = x;
+}
+
 }  // namespace
+
+hipError_t launch_bench_mfma(const void* operands, int workgroups, int iters, float* sink, hipStream_t stream) {
+  hipLaunchKernelGGL(mfma_kernel, dim3(workgroups), dim3(512), 0, stream, (const u32x4*)operands, iters, sink);
+  return hipGetLastError();
+}
 
 hipError_t launch_bench_copy(void* dst, const void* src, size_t bytes, hipStream_t stream) {
   const int64_t n = (int64_t)(bytes / 16);

@@ -724,6 +724,12 @@ int pa_bench_read(const void* src, size_t bytes, float* sink, void* stream) {
   return hip_status(pa::launch_bench_read(src, bytes, sink, as_stream(stream)), "read launch");
 }
 
+int pa_bench_mfma(const void* operands, int32_t workgroups, int32_t iters, float* sink, void* stream) {
+  if (!operands || !sink || workgroups <= 0 || iters < 0)
+    return fail(PA_ERR_INVALID_ARG, "mfma needs operands, a sink, workgroups > 0 and iters >= 0");
+  return hip_status(pa::launch_bench_mfma(operands, workgroups, iters, sink, as_stream(stream)), "mfma launch");
+}
+
 int pa_bench_flush(void* buf, size_t bytes, void* stream) {
   if (!buf || bytes % 16) return fail(PA_ERR_INVALID_ARG, "flush needs 16-byte multiples");
   if (bytes == 0) return PA_OK;

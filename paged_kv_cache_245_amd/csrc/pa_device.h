@@ -189,5 +189,6 @@ hipError_t launch_swap_blocks(void* k_cache, void* v_cache, void* host_k, void* 
 hipError_t launch_bench_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
 hipError_t launch_bench_read(const void* src, size_t bytes, float* sink, hipStream_t stream);
 hipError_t launch_bench_flush(void* buf, size_t bytes, hipStream_t stream);
+hipError_t launch_bench_mfma(const void* operands, int workgroups, int iters, float* sink, hipStream_t stream);
 
 }  // namespace pa

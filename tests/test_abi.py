@@ -167,6 +167,8 @@ def test_bench_argument_checks(lib):
     fake = ctypes.c_void_p(0x1000)
     assert lib.pa_bench_copy(fake, fake, 17, None) == INVALID
     assert lib.pa_bench_flush(None, 32, None) == INVALID
+    assert lib.pa_bench_mfma(None, 1, 1, fake, None) == INVALID
+    assert lib.pa_bench_mfma(fake, 0, 1, fake, None) == INVALID
 
 
 def test_binding_refuses_host_tensors(lib):
