@@ -10,6 +10,7 @@
 // device current, and only that address is handed to the kernels.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <mutex>
 #include <string>
 
@@ -21,8 +22,8 @@ static __device__ __align__(256) unsigned char scratch[PA_NOALLOC_SCRATCH_BYTES]
 namespace {
 
 constexpr int kMaxDevices = 64;
-void* g_scratch[kMaxDevices];  // device address of `scratch` on each device, once looked up
-std::mutex g_scratch_mu;
+std::atomic<void*> g_scratch[kMaxDevices];  // device address of `scratch` on each device, once looked up
+std::mutex g_scratch_mu;                    // serialises the first lookups
 
 // Device address of the current device's `scratch`; PA_OK or a negative status.
 int scratch_address(void** out) {
@@ -34,18 +35,21 @@ int scratch_address(void** out) {
   }
   if (dev < 0 || dev >= kMaxDevices)
     return pa::set_error_detail(PA_ERR_UNSUPPORTED, "device index above 63");
-  std::lock_guard<std::mutex> lock(g_scratch_mu);
-  if (g_scratch[dev] == nullptr) {
-    void* p = nullptr;
-    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
-    if (e != hipSuccess || p == nullptr) {
-      (void)hipGetLastError();
-      return pa::set_error_detail(
-          PA_ERR_HIP, (std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e)).c_str());
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || p == nullptr) {
+        (void)hipGetLastError();
+        return pa::set_error_detail(
+            PA_ERR_HIP, (std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e)).c_str());
+      }
+      g_scratch[dev].store(p, std::memory_order_release);
     }
-    g_scratch[dev] = p;
   }
-  *out = g_scratch[dev];
+  *out = p;
   return PA_OK;
 }
 
