@@ -46,11 +46,13 @@
 // through the block table. No workgroup reads a new token's slot, so the stores
 // need no ordering against the reads; the rows are loaded before the first
 // tiles and stored after the first barrier.
-// Work items (request, kv head, query tile) run heaviest first: workgroup i of
-// the dispatch order takes the item of rank i by cost (see item_of_rank).
-// Within one cost level consecutive workgroups take the kv heads of one
-// (request, tile) in turn, so with 8 kv heads each XCD (which receives every
-// 8th workgroup) keeps serving the same kv head's K/V from its L2.
+// Work items (request, kv head, query tile) run request by request, the
+// heaviest request first and its query tiles heaviest first: workgroup i of the
+// dispatch order takes the item of rank i (see item_of_rank). Consecutive
+// workgroups take the kv heads of one (request, tile) in turn, so with 8 kv
+// heads each XCD (which receives every 8th workgroup) serves one kv head's K/V
+// from its L2, and the query tiles of one request start together and read the
+// same keys at about the same time.
 #include <type_traits>
 
 #include "pa_device.h"
@@ -93,13 +95,17 @@ __device__ __forceinline__ int v_phys(int row, int ch) {
 }
 
 // Work items are (request, kv head, query tile); an item's cost is the number
-// of 64-key tiles it reads, ceil((cached + min((tile + 1) kPos, nq)) / 64). The
-// launch runs items heaviest first (longest-processing-time order): workgroup
-// number i (in dispatch order) takes the item of rank i in non-increasing cost,
-// ties broken by (request, query tile, kv head). Each workgroup finds its item
-// itself from the requests' lengths: a binary search on the cost level c with
-// count(c) = items of cost >= c, which is closed-form per request because cost
-// grows with the query tile.
+// of 64-key tiles it reads, ceil((cached + min((tile + 1) kPos, nq)) / 64), and a
+// request's level is the cost of its heaviest tile, ceil((cached + nq) / 64).
+// Items run request by request, in non-increasing level (ties by request
+// index); within a request, query tiles from the last (heaviest) to the first,
+// the kv heads of each tile in turn. Grouping by request keeps the K/V of few
+// requests in flight on each XCD's L2 at once: ordering single items heaviest
+// first interleaves every request's tiles over the whole launch, and tiles of
+// one (request, kv head) that start far apart in time re-read its K/V from
+// beyond the L2. Ordering requests by level keeps the longest-first balance.
+// Each workgroup finds its item itself from the requests' lengths: a binary
+// search on the level c with count(c) = items of requests of level >= c.
 struct ReqShape {
   int nq, cached, tiles;  // rows of the chunk, cached keys, query tiles (0: no work)
 };
@@ -120,13 +126,8 @@ __device__ __forceinline__ ReqShape req_shape(const PrefillArgs& a, int r, int k
   return q;
 }
 
-// First query tile of a request whose cost is >= c (tiles when there is none).
-__device__ __forceinline__ int first_tile_ge(const ReqShape& q, int c, int kPos) {
-  const int64_t rest = 64LL * (c - 1) - q.cached;
-  if (rest < 0) return 0;
-  if (q.nq <= rest) return q.tiles;
-  return (int)min<int64_t>(rest / kPos, q.tiles);
-}
+// Level of a request with work: the cost of its heaviest (last) query tile.
+__device__ __forceinline__ int req_level(const ReqShape& q) { return (q.cached + q.nq + 63) / 64; }
 
 __device__ __forceinline__ int64_t wave_sum_i64(int64_t v) {
 #pragma unroll
@@ -134,40 +135,41 @@ __device__ __forceinline__ int64_t wave_sum_i64(int64_t v) {
   return v;
 }
 
-// Items of cost >= c over all requests (one wavefront, lanes over requests).
-__device__ int64_t items_cost_ge(const PrefillArgs& a, int c, int kPos, int lane) {
+// Items of requests of level >= c (one wavefront, lanes over requests).
+__device__ int64_t items_level_ge(const PrefillArgs& a, int c, int kPos, int lane) {
   int64_t acc = 0;
   for (int r = lane; r < a.num_seqs; r += 64) {
     const ReqShape q = req_shape(a, r, kPos);
-    acc += (int64_t)a.num_kv_heads * (q.tiles - first_tile_ge(q, c, kPos));
+    if (q.tiles > 0 && req_level(q) >= c) acc += (int64_t)a.num_kv_heads * q.tiles;
   }
   return wave_sum_i64(acc);
 }
 
-// The item of rank `rank` in heaviest-first order, as (request, kv head, tile),
-// or request -1 when rank >= the number of items. Run by one whole wavefront;
+// The item of rank `rank` in the order above, as (request, kv head, tile), or
+// request -1 when rank >= the number of items. Run by one whole wavefront;
 // every lane gets the result.
 __device__ void item_of_rank(const PrefillArgs& a, int64_t rank, int kPos, int lane, int out[3]) {
   out[0] = -1;
   out[1] = out[2] = 0;
-  if (items_cost_ge(a, 1, kPos, lane) <= rank) return;
-  int lo = 1, hi = (a.max_seq_len + 63) / 64 + 1;  // count(lo) > rank >= count(hi)
+  if (items_level_ge(a, 1, kPos, lane) <= rank) return;
+  // a level is at most ceil(max(L, nq) / 64) over the clamped lengths
+  int lo = 1, hi = (max(a.max_seq_len, a.max_query_len) + 63) / 64 + 1;  // count(lo) > rank >= count(hi)
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (items_cost_ge(a, mid, kPos, lane) > rank) lo = mid;
+    if (items_level_ge(a, mid, kPos, lane) > rank) lo = mid;
     else hi = mid;
   }
   const int c = lo;
-  const int64_t j = rank - items_cost_ge(a, c + 1, kPos, lane);  // rank among items of cost c
+  const int64_t j = rank - items_level_ge(a, c + 1, kPos, lane);  // rank among requests of level c
   int64_t acc = 0;
   for (int base = 0; base < a.num_seqs; base += 64) {
     const int r = base + lane;
     int64_t n = 0;
-    int f0 = 0;
+    int tiles = 0;
     if (r < a.num_seqs) {
       const ReqShape q = req_shape(a, r, kPos);
-      f0 = first_tile_ge(q, c, kPos);
-      n = (int64_t)a.num_kv_heads * (first_tile_ge(q, c + 1, kPos) - f0);
+      tiles = q.tiles;
+      if (q.tiles > 0 && req_level(q) == c) n = (int64_t)a.num_kv_heads * q.tiles;
     }
     int64_t incl = n;  // inclusive prefix sum over the lanes
 #pragma unroll
@@ -181,7 +183,7 @@ __device__ void item_of_rank(const PrefillArgs& a, int64_t rank, int kPos, int l
       const int64_t off = j - (acc + incl - n);  // meaningful on lane src
       out[0] = __shfl(r, src, 64);
       out[1] = __shfl((int)(off % a.num_kv_heads), src, 64);
-      out[2] = __shfl(f0 + (int)(off / a.num_kv_heads), src, 64);
+      out[2] = __shfl(tiles - 1 - (int)(off / a.num_kv_heads), src, 64);
       return;
     }
     acc += __shfl(incl, 63, 64);

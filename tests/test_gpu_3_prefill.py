@@ -79,9 +79,9 @@ def test_empty_chunk_is_skipped():
     assert not out[5:].any()
 
 
-def test_many_requests_heaviest_first_order():
-    """150 chunks of mixed sizes: the in-kernel heaviest-first work order walks the requests
-    64 at a time, and every row must still be computed exactly once."""
+def test_many_requests_work_order():
+    """150 chunks of mixed sizes: the in-kernel work order (requests longest first) walks the
+    requests 64 at a time, and every row must still be computed exactly once."""
     rng = np.random.default_rng(81)
     new = rng.integers(1, 41, 150)
     new[::17] = 1
@@ -146,7 +146,7 @@ def test_append_shapes(group, D):
 
 
 def test_append_many_requests():
-    """150 chunks of mixed sizes and offsets (the heaviest-first order over many requests)."""
+    """150 chunks of mixed sizes and offsets (the work order over many requests)."""
     rng = np.random.default_rng(82)
     new = rng.integers(1, 41, 150)
     cached = rng.integers(0, 301, 150)
