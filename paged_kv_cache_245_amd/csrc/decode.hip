@@ -598,11 +598,11 @@ constexpr int kMergeHeads = 8;
 // Partials are read eight at a time, all loads of a batch issued before any use,
 // and folded into a running (M, den, o) rescaled to the batch maximum.
 // kTwo: partials np .. np + np2 - 1 come from a second list, rows row2 + i of
-// acc2 / ml2, folded in the same batches as the first list's.
+// acc2 / ml2 (accumulators in bf16), folded in the same batches as the first list's.
 template <int D, bool kTwo = false>
 __device__ __forceinline__ void fold_partials(const float* part_acc, const float* part_ml, int64_t row0,
                                               int64_t rstep, int np, int lane, float (&o)[D / 64], float& den,
-                                              float& M, const float* acc2 = nullptr, const float* ml2 = nullptr,
+                                              float& M, const uint16_t* acc2 = nullptr, const float* ml2 = nullptr,
                                               int64_t row2 = 0, int np2 = 0) {
   constexpr int kE = D / 64;
   constexpr int kBatch = 8;
@@ -618,13 +618,24 @@ __device__ __forceinline__ void fold_partials(const float* part_acc, const float
       const int i = i0 + j;
       const bool in = i < n, second = kTwo && i >= np;
       const float* ml = second ? ml2 : part_ml;
-      const float* acc = second ? acc2 : part_acc;
       const int64_t r = !in ? row0 : second ? row2 + (i - np) : row0 + (int64_t)i * rstep;
       mi[j] = in ? ml[2 * r] : -INFINITY;
       li[j] = in ? ml[2 * r + 1] : 0.f;
-      const float* src = acc + r * D + kE * lane;
+      if constexpr (kTwo) {
+        // both lists' rows are read (the unused one is a row the fold reads anyway)
+        // and one is selected, so no branch holds back the batch's loads
+        const float* src = part_acc + (second ? row0 : r) * D + kE * lane;
+        const uint16_t* src2 = acc2 + (second ? r : row2) * D + kE * lane;
 #pragma unroll
-      for (int e = 0; e < kE; ++e) ai[j][e] = in ? src[e] : 0.f;
+        for (int e = 0; e < kE; ++e) {
+          const float v1 = src[e], v2 = bf16_bits_to_f32(src2[e]);
+          ai[j][e] = !in ? 0.f : second ? v2 : v1;
+        }
+      } else {
+        const float* src = part_acc + r * D + kE * lane;
+#pragma unroll
+        for (int e = 0; e < kE; ++e) ai[j][e] = in ? src[e] : 0.f;
+      }
     }
     float mb = M;
 #pragma unroll
@@ -840,7 +851,9 @@ __global__ __launch_bounds__(kWideThreads) void decode_merge_wide_kernel(DecodeA
     for (int j = 0; j < a.pre_parts; ++j) {
       const float mj = a.pre_ml[2 * (p0 + j)];
       const float lj = a.pre_ml[2 * (p0 + j) + 1];
-      const f32x4 aj = *(const f32x4*)(a.pre_acc + (p0 + j) * D + 4 * ti);
+      const u32x2 bj = *(const u32x2*)(a.pre_acc + (p0 + j) * D + 4 * ti);  // 4 bf16
+      const f32x4 aj = {bf16_bits_to_f32(bj[0] & 0xffffu), bf16_bits_to_f32(bj[0] >> 16),
+                        bf16_bits_to_f32(bj[1] & 0xffffu), bf16_bits_to_f32(bj[1] >> 16)};
       const float mb = fmaxf(M2, mj);
       const float alpha = fast_exp2(M2 - mb), wgt = fast_exp2(mj - mb);
       den2 = den2 * alpha + wgt * lj;

@@ -211,7 +211,7 @@ PrefixLayout prefix_layout(const pa_cache_desc* d, int32_t num_seqs, int32_t max
   p.splits = (int32_t)std::max<int64_t>(1, (keys + p.key_chunk - 1) / p.key_chunk);
   const size_t rows = (size_t)num_seqs * d->num_q_heads * p.splits;
   p.acc_offset = align256(p.dec.total);
-  p.ml_offset = p.acc_offset + align256(rows * d->head_dim * sizeof(float));
+  p.ml_offset = p.acc_offset + align256(rows * d->head_dim * sizeof(uint16_t));  // bf16 accumulators
   p.total = p.ml_offset + align256(rows * 2 * sizeof(float));
   return p;
 }
@@ -407,7 +407,7 @@ int decode_impl(const pa_cache_desc* desc, void* out, const void* q, const void*
     pf.prefix_keys = prefix_blocks * PA_BLOCK_SIZE;
     pf.key_chunk = play.key_chunk;
     pf.key_splits = play.splits;
-    pf.part_acc = (float*)((char*)workspace + play.acc_offset);
+    pf.part_acc = (uint16_t*)((char*)workspace + play.acc_offset);
     pf.part_ml = (float*)((char*)workspace + play.ml_offset);
     st = hip_status(pa::launch_prefix_attention(pf, desc->head_dim, a.group, as_stream(stream)),
                     "prefix launch");

@@ -109,11 +109,11 @@ struct DecodeArgs {
   // Shared-prefix mode (balanced only): every request's first skip_blocks blocks
   // are not read; every segment leaves a partial (partial_only); and the merge
   // also folds pre_parts partials per (request, q head) from pre_acc / pre_ml
-  // (laid out as PrefillArgs' part_acc / part_ml).
+  // (laid out as PrefillArgs' part_acc / part_ml; the accumulators in bf16).
   int32_t skip_blocks;
   int32_t partial_only;
   int32_t pre_parts;
-  const float* pre_acc;
+  const uint16_t* pre_acc;
   const float* pre_ml;
 };
 
@@ -138,12 +138,14 @@ struct PrefillArgs {
   // queries q [num_seqs][Hq][D], all attending the first prefix_keys keys of
   // block table row 0 with no causal mask; the keys are split into key_splits
   // ranges of key_chunk (a multiple of 64), and each (request, q head, range)
-  // leaves a partial (m, l, acc) instead of an output.
+  // leaves a partial (m, l, acc) instead of an output. acc (the weighted sum of
+  // V rows, not divided by l) is stored in bf16, rounded to nearest even, as the
+  // outputs are: it halves the bytes the pass writes and the merge reads.
   int32_t prefix_keys;
   int32_t key_chunk;
   int32_t key_splits;
-  float* part_acc;  // [num_seqs][Hq][key_splits][D]
-  float* part_ml;   // [num_seqs][Hq][key_splits][2]
+  uint16_t* part_acc;  // [num_seqs][Hq][key_splits][D] bf16
+  float* part_ml;      // [num_seqs][Hq][key_splits][2]
   // Append mode (launch_prefill with both set): [num_tokens][Hkv][D] K and V of
   // the chunks' own tokens, row t for query row t. The kernel reads a chunk's keys
   // from here instead of the pool, and each workgroup stores the rows of its own

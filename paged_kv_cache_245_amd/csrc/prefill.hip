@@ -544,13 +544,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
   if constexpr (kCross) {
     // partial (m, l, acc) of row (request pos, q head h) over key range blockIdx.y
     const int64_t pidx = ((int64_t)pos * a.num_q_heads + h) * a.key_splits + blockIdx.y;
-    float* dst = a.part_acc + pidx * D;
+    uint16_t* dst = a.part_acc + pidx * D;  // acc in bf16 (not divided by l)
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
       for (int grp = 0; grp < 4; ++grp)  // o[dt][4 grp + i] is dim 32 dt + 8 grp + 4 half + i
-        *(f32x4*)(dst + 32 * dt + 8 * grp + 4 * half) =
-            f32x4{o[dt][4 * grp], o[dt][4 * grp + 1], o[dt][4 * grp + 2], o[dt][4 * grp + 3]};
+        *(u32x2*)(dst + 32 * dt + 8 * grp + 4 * half) =
+            u32x2{pack_bf16x2(o[dt][4 * grp], o[dt][4 * grp + 1]), pack_bf16x2(o[dt][4 * grp + 2], o[dt][4 * grp + 3])};
     if (half == 0) {
       a.part_ml[2 * pidx] = m;
       a.part_ml[2 * pidx + 1] = poisoned ? __builtin_nanf("") : lsum;
