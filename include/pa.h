@@ -256,9 +256,9 @@ int pa_decode_append_noalloc(const pa_cache_desc* desc, void* out, const void* q
  * read once for all requests: its attention runs as one dense pass over all the
  * requests' queries on the matrix cores, split into key ranges. Only each
  * request's remaining blocks go through the split-KV decode, and the merge
- * combines both (each key range's weighted sum of V rows passes to the merge
- * rounded to bf16, its max and sum of exponentials in float32; the tails' partials
- * stay float32). Sharing full blocks between requests through the prefix cache
+ * combines both (each key range's and each tail segment's weighted sum of V rows
+ * passes to the merge rounded to bf16, its max and sum of exponentials in
+ * float32). Sharing full blocks between requests through the prefix cache
  * is arcyou teardown, "PagedAttention: the KV cache is paged, like virtual
  * memory"; the result is attention over each request's whole logical context.
  *   prefix_blocks   0 (then this is pa_decode) or the number of shared blocks;

@@ -203,17 +203,30 @@ __device__ __forceinline__ void store_final(uint16_t* O, int64_t qo_row, const f
   }
 }
 
-template <int D>
+// The partial (m, l, acc) of one (segment, q head). kBf16 (shared-prefix mode,
+// its own kernel instantiation): acc is stored in bf16 (rounded to nearest
+// even), as the prefix pass stores its own, so the merge reads both lists alike,
+// at half the bytes.
+template <int D, bool kBf16 = false>
 __device__ __forceinline__ void store_partial(const DecodeArgs& a, int64_t pidx, const f32x4* acc,
                                               float m, float lsum, int g4) {
   constexpr int kDL = D / 16;
-  float* dst = a.part_acc + pidx * D;
+  if constexpr (kBf16) {
+    uint32_t* dst = (uint32_t*)((uint16_t*)a.part_acc + pidx * D);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int t4 = 0; t4 < kDL; t4 += 4)
-      *(f32x4*)(dst + kDL * (4 * g4 + i) + t4) =
-          f32x4{acc[t4][i], acc[t4 + 1][i], acc[t4 + 2][i], acc[t4 + 3][i]};
+      for (int t2 = 0; t2 < kDL; t2 += 2)
+        dst[(kDL * (4 * g4 + i) + t2) / 2] = pack_bf16x2(acc[t2][i], acc[t2 + 1][i]);
+  } else {
+    float* dst = a.part_acc + pidx * D;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int t4 = 0; t4 < kDL; t4 += 4)
+        *(f32x4*)(dst + kDL * (4 * g4 + i) + t4) =
+            f32x4{acc[t4][i], acc[t4 + 1][i], acc[t4 + 2][i], acc[t4 + 3][i]};
+  }
   if (g4 == 0) {
     a.part_ml[2 * pidx] = m;
     a.part_ml[2 * pidx + 1] = lsum;
@@ -223,7 +236,7 @@ __device__ __forceinline__ void store_partial(const DecodeArgs& a, int64_t pidx,
 // One wavefront attends keys of blocks [blk_a, blk_b) of request s (kv head kvh),
 // keys limited to the first `end_tok` tokens, and writes the final output (whole)
 // or the partial state into partial row pidx_base + q head.
-template <int D, bool kNT>
+template <int D, bool kNT, bool kBf16 = false>
 __device__ __forceinline__ void decode_segment(const DecodeArgs& a, int s, int kvh, int blk_a,
                                                int blk_b, int end_tok, bool whole,
                                                int64_t pidx_base, int64_t pidx_stride) {
@@ -297,7 +310,7 @@ __device__ __forceinline__ void decode_segment(const DecodeArgs& a, int s, int k
   if (whole)
     store_final<D>((uint16_t*)a.out, qo_row, acc, lsum, g4);
   else
-    store_partial<D>(a, pidx_base + (int64_t)h * pidx_stride, acc, m, lsum, g4);
+    store_partial<D, kBf16>(a, pidx_base + (int64_t)h * pidx_stride, acc, m, lsum, g4);
 }
 
 // Lean variant of decode_segment, for a decode that shares compute units with a
@@ -460,7 +473,7 @@ __device__ __forceinline__ int request_blocks(const DecodeArgs& a, int s) {
 // kAppend: the pool is read up to each request's newest token and every segment
 // leaves a partial, which the merge combines with the newest key.
 // kLean: one wavefront per workgroup, segments through decode_segment_lean.
-template <int D, int NW, bool kAppend, bool kLean>
+template <int D, int NW, bool kAppend, bool kLean, bool kBf16 = false>
 __device__ __forceinline__ void balanced_body(const DecodeArgs& a) {
   extern __shared__ int32_t cum[];
   __shared__ u32x4 q_lds[kLean ? (D / 32) * 64 : 1];  // the lean segments' query operands
@@ -551,9 +564,9 @@ __device__ __forceinline__ void balanced_body(const DecodeArgs& a) {
           decode_segment_lean<D, false>(a, s, kvh, b0, b1, n_keys, whole, slot * a.num_q_heads, 1, q_lds);
       } else {
         if (nt)
-          decode_segment<D, true>(a, s, kvh, b0, b1, n_keys, whole, slot * a.num_q_heads, 1);
+          decode_segment<D, true, kBf16>(a, s, kvh, b0, b1, n_keys, whole, slot * a.num_q_heads, 1);
         else
-          decode_segment<D, false>(a, s, kvh, b0, b1, n_keys, whole, slot * a.num_q_heads, 1);
+          decode_segment<D, false, kBf16>(a, s, kvh, b0, b1, n_keys, whole, slot * a.num_q_heads, 1);
       }
       pos = seg_end;
     }
@@ -561,9 +574,9 @@ __device__ __forceinline__ void balanced_body(const DecodeArgs& a) {
   }
 }
 
-template <int D, int NW, bool kAppend>
+template <int D, int NW, bool kAppend, bool kBf16 = false>
 __global__ __launch_bounds__(64 * NW) void decode_bf16_balanced_kernel(DecodeArgs a) {
-  balanced_body<D, NW, kAppend, false>(a);
+  balanced_body<D, NW, kAppend, false, kBf16>(a);
 }
 
 // The lean decode: grid (W, kv heads), one wavefront each, within 96 registers so
@@ -597,8 +610,9 @@ constexpr int kMergeHeads = 8;
 // o = sum_i 2^(m_i - M) acc_i and den = sum_i 2^(m_i - M) l_i; the caller divides.
 // Partials are read eight at a time, all loads of a batch issued before any use,
 // and folded into a running (M, den, o) rescaled to the batch maximum.
-// kTwo: partials np .. np + np2 - 1 come from a second list, rows row2 + i of
-// acc2 / ml2 (accumulators in bf16), folded in the same batches as the first list's.
+// kTwo (shared-prefix mode): partials np .. np + np2 - 1 come from a second
+// list, rows row2 + i of acc2 / ml2, folded in the same batches as the first
+// list's; both lists then hold their accumulators in bf16.
 template <int D, bool kTwo = false>
 __device__ __forceinline__ void fold_partials(const float* part_acc, const float* part_ml, int64_t row0,
                                               int64_t rstep, int np, int lane, float (&o)[D / 64], float& den,
@@ -622,15 +636,11 @@ __device__ __forceinline__ void fold_partials(const float* part_acc, const float
       mi[j] = in ? ml[2 * r] : -INFINITY;
       li[j] = in ? ml[2 * r + 1] : 0.f;
       if constexpr (kTwo) {
-        // both lists' rows are read (the unused one is a row the fold reads anyway)
-        // and one is selected, so no branch holds back the batch's loads
-        const float* src = part_acc + (second ? row0 : r) * D + kE * lane;
-        const uint16_t* src2 = acc2 + (second ? r : row2) * D + kE * lane;
+        // the row's list is selected by pointer, so no branch holds back the
+        // batch's loads
+        const uint16_t* src = (second ? acc2 : (const uint16_t*)part_acc) + r * D + kE * lane;
 #pragma unroll
-        for (int e = 0; e < kE; ++e) {
-          const float v1 = src[e], v2 = bf16_bits_to_f32(src2[e]);
-          ai[j][e] = !in ? 0.f : second ? v2 : v1;
-        }
+        for (int e = 0; e < kE; ++e) ai[j][e] = in ? bf16_bits_to_f32(src[e]) : 0.f;
       } else {
         const float* src = part_acc + r * D + kE * lane;
 #pragma unroll
@@ -757,7 +767,7 @@ __global__ __launch_bounds__(64 * kMergeHeads) void decode_merge_balanced_kernel
 // block id) is requested first.
 constexpr int kWideThreads = 1024;
 
-template <int D, bool kAppend>
+template <int D, bool kAppend, bool kBf16Parts = false>
 __global__ __launch_bounds__(kWideThreads) void decode_merge_wide_kernel(DecodeArgs a) {
   constexpr int kT = D / 4;              // threads per group, one float4 of dims each
   constexpr int kG = kWideThreads / kT;  // groups
@@ -805,7 +815,13 @@ __global__ __launch_bounds__(kWideThreads) void decode_merge_wide_kernel(DecodeA
       const int64_t r = row0 + (int64_t)(in ? i : 0) * rstep;
       mi[j] = in ? a.part_ml[2 * r] : -INFINITY;
       li[j] = in ? a.part_ml[2 * r + 1] : 0.f;
-      ai[j] = in ? *(const f32x4*)(a.part_acc + r * D + 4 * ti) : f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (kBf16Parts) {  // shared-prefix mode: bf16 accumulators
+        const u32x2 b = in ? *(const u32x2*)((const uint16_t*)a.part_acc + r * D + 4 * ti) : u32x2{0, 0};
+        ai[j] = f32x4{bf16_bits_to_f32(b[0] & 0xffffu), bf16_bits_to_f32(b[0] >> 16),
+                      bf16_bits_to_f32(b[1] & 0xffffu), bf16_bits_to_f32(b[1] >> 16)};
+      } else {
+        ai[j] = in ? *(const f32x4*)(a.part_acc + r * D + 4 * ti) : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
     }
     float mb = M;
 #pragma unroll
@@ -1099,6 +1115,9 @@ void launch_bf16_nw(const DecodeArgs& a, hipStream_t stream) {
     if (a.new_k != nullptr)
       hipLaunchKernelGGL((decode_bf16_balanced_kernel<D, NW, true>), dim3(a.num_workers, groups),
                          dim3(64 * NW), lds, stream, a);
+    else if (a.partial_only)  // shared-prefix mode: bf16 partials
+      hipLaunchKernelGGL((decode_bf16_balanced_kernel<D, NW, false, true>), dim3(a.num_workers, groups),
+                         dim3(64 * NW), lds, stream, a);
     else
       hipLaunchKernelGGL((decode_bf16_balanced_kernel<D, NW, false>), dim3(a.num_workers, groups),
                          dim3(64 * NW), lds, stream, a);
@@ -1137,6 +1156,8 @@ hipError_t launch_decode_d(const DecodeArgs& args, bool bf16, hipStream_t stream
     const bool wide = a.num_workers > 8 * a.num_seqs;
     if (wide && a.new_k != nullptr)
       hipLaunchKernelGGL((decode_merge_wide_kernel<D, true>), mgrid, dim3(kWideThreads), 0, stream, a);
+    else if (wide && a.partial_only)
+      hipLaunchKernelGGL((decode_merge_wide_kernel<D, false, true>), mgrid, dim3(kWideThreads), 0, stream, a);
     else if (wide)
       hipLaunchKernelGGL((decode_merge_wide_kernel<D, false>), mgrid, dim3(kWideThreads), 0, stream, a);
     else if (a.new_k != nullptr)

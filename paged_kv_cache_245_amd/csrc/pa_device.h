@@ -80,7 +80,7 @@ struct DecodeArgs {
   void* out;
   const int32_t* block_tables;
   const int32_t* context_lens;
-  float* part_acc;  // [S][Hq][max_parts][D]
+  float* part_acc;  // [S][Hq][max_parts][D] (bf16 values, D per row, in shared-prefix mode)
   float* part_ml;   // [S][Hq][max_parts][2]: running max (log2 units), sum of exponentials
   int64_t num_blocks;
   int32_t max_blocks;
