@@ -43,9 +43,14 @@
 //   Scores are in log2 units (scale * log2 e), so each exponential is v_exp_f32.
 // The next pair's K/V is loaded before the current pair is used (two register
 // buffers), and a segment's block ids are fetched 64 at a time into one VGPR.
+// In balanced mode a worker streams its segments back to back: the next
+// segment's first pair is issued while the current segment's last pair is
+// attended, and segment results are staged in LDS and written after the
+// worker's last segment (see stream_range).
 //
 // fp32 pools use a plain VALU kernel (lanes over keys for q.k, lanes over dims
 // for PV) in fixed-partition mode.
+#include <algorithm>
 #include <cstdlib>
 
 #include "pa_device.h"
@@ -469,10 +474,259 @@ __device__ __forceinline__ int request_blocks(const DecodeArgs& a, int s) {
   return n > 0 ? max(((n + 15) >> 4) - a.skip_blocks, 0) : 0;
 }
 
-// Balanced mode: grid (W, kv-head groups); dynamic LDS holds S+1 ints.
+// Segment results wait in LDS until the worker's range is done. Vector-memory
+// operations retire in order, so a store holds up every later wait on a load
+// until the store is acknowledged; under a full read stream that costs several
+// microseconds per store, once per segment. Staged, the stores all go out after
+// the last load is used. Each wavefront has kRingBytesPerWave of LDS, filled
+// front to back with records: a 16-byte header (request; top bit set for a
+// whole request), then for a whole request the final bf16 words of its 4 G
+// lanes (what store_final writes), else their fp32 acc followed by (m, l) per
+// head. A segment whose record does not fit any more is stored directly. The
+// host sizes the buffer (a.ring_bytes per wavefront, at most kRingCapPerWave)
+// so that the workgroups the kernel's registers admit on a compute unit still
+// fit its LDS beside their prefix sums.
+constexpr int kRingCapPerWave = 15 * 1024;
+__host__ __device__ constexpr size_t ring_offset(int S) { return ((size_t)(S + 1) * 4 + 15) & ~(size_t)15; }
+
+// A worker's whole block range [lo, hi) for one kv head, segment after segment,
+// with the next segment's first pair of blocks issued while the current
+// segment's last pair is attended (decode_segment starts each segment cold:
+// block ids, then the first pair, then the products). The issue cursor runs
+// one pair ahead of the attend cursor, so it is in the attended segment or the
+// one after it; the block ids of the segment after the issue cursor's are
+// fetched when the cursor enters a segment.
+template <int D, bool kNT, bool kAppend, bool kBf16>
+__device__ __forceinline__ void stream_range(const DecodeArgs& a, const int32_t* cum, int first, int lo,
+                                             int hi, int w, int kvh) {
+  constexpr int kChunks = D / 32;
+  constexpr int kDL = D / 16;
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 15;
+  const int g4 = lane >> 4;
+  const int G = a.group;
+  const int Hkv = a.num_kv_heads;
+  const int h = kvh * G + n;
+  const bool head_ok = n < G;
+  const uint16_t* __restrict__ K = (const uint16_t*)a.k;
+  const uint16_t* __restrict__ V = (const uint16_t*)a.v;
+  const LaneOffsets offs = lane_offsets<D>(kvh, Hkv, n, g4);
+
+  // segment of request s (or a later one) that starts at pos: table indices [b0, b1)
+  struct Span { int s, b0, b1, end; };
+  auto span_from = [&](int s, int pos) {
+    while (__builtin_amdgcn_readfirstlane(cum[s + 1]) <= pos) ++s;
+    const int cs = __builtin_amdgcn_readfirstlane(cum[s]);
+    const int ce = __builtin_amdgcn_readfirstlane(cum[s + 1]);
+    Span r;
+    r.s = s;
+    r.end = min(ce, hi);
+    r.b0 = a.skip_blocks + pos - cs;
+    r.b1 = a.skip_blocks + r.end - cs;
+    return r;
+  };
+  auto ids_of = [&](const Span& sp, int base) -> int32_t {
+    const int32_t* table = a.block_tables + (int64_t)sp.s * a.max_blocks;
+    return (lane < sp.b1 - base) ? table[base + lane] : 0;
+  };
+
+  // attend cursor: segment A, next block ab
+  Span A = span_from(first, lo);
+  int ab = A.b0;
+  int end_tok = min(pool_keys<kAppend>(a, A.s), 16 * A.b1);
+  bool whole = !kAppend && !a.partial_only && lo == __builtin_amdgcn_readfirstlane(cum[A.s]) &&
+               A.end == __builtin_amdgcn_readfirstlane(cum[A.s + 1]);
+  // issue cursor: segment I (starts as A), next block ib, its ids idv from ibase;
+  // the segment N after I and its first ids
+  Span I = A;
+  int ib = I.b0, ibase = I.b0;
+  int32_t idv = ids_of(I, ibase);
+  bool has_n = I.end < hi, i_live = true;
+  Span N = I;
+  int32_t idv_n = 0;
+  if (has_n) {
+    N = span_from(I.s + 1, I.end);
+    idv_n = ids_of(N, N.b0);
+  }
+  bool pois_a = false, pois_next = false;
+
+  u32x4 qb[kChunks];
+  auto load_q = [&](int s) {
+    const int64_t qo_row = ((int64_t)s * a.num_q_heads + h) * D;
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c)
+      qb[c] = head_ok ? *(const u32x4*)((const uint16_t*)a.q + qo_row + 32 * c + 8 * g4) : u32x4{0, 0, 0, 0};
+  };
+  load_q(A.s);
+  f32x4 acc[kDL];
+#pragma unroll
+  for (int t = 0; t < kDL; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, lsum = 0.f;
+
+  auto block_id = [&](int b) -> int32_t {
+    if (b - ibase >= 64) {
+      ibase += 64;
+      idv = ids_of(I, ibase);
+    }
+    int32_t id = __builtin_amdgcn_readlane(idv, b - ibase);
+    if (!block_ok(id, a.num_blocks)) {
+      if (I.s == A.s) pois_a = true; else pois_next = true;
+      id = 0;
+    }
+    return id;
+  };
+  // issue the pair at the issue cursor, then move the cursor on
+  auto issue_next = [&](Tile<D>& t) {
+    if (!i_live) return;
+    const bool two = ib + 1 < I.b1;
+    const int32_t id0 = block_id(ib);
+    const int32_t id1 = two ? block_id(ib + 1) : 0;
+    load_pair<D, kNT>(t, K, V, id0, id1, two, offs);
+    ib += 2;
+    if (ib >= I.b1) {
+      if (has_n) {
+        I = N;
+        ib = I.b0;
+        ibase = I.b0;
+        idv = idv_n;
+        has_n = I.end < hi;
+        if (has_n) {
+          N = span_from(I.s + 1, I.end);
+          idv_n = ids_of(N, N.b0);
+        }
+      } else {
+        i_live = false;
+      }
+    }
+  };
+  // attend the pair at the attend cursor; at the end of segment A, store it and
+  // move A on (returns false after the worker's last segment)
+  // this wavefront's records, after the prefix sums; written out after the last segment
+  constexpr int kWordsFinal = D / 32;             // u32 words per (lane, row group i) of a final
+  const int li = n * 4 + g4;                      // record row of this lane (n < G)
+  const int final_bytes = 16 + 4 * G * (4 * kWordsFinal * 4);
+  const int part_bytes = (16 + 4 * G * (16 * kDL) + 8 * G + 15) & ~15;  // records stay 16-byte aligned
+  const int ring_bytes = a.ring_bytes;
+  char* ring = (char*)cum + ring_offset(a.num_seqs) + (size_t)(threadIdx.x >> 6) * ring_bytes;
+  int used = 0;  // bytes of records (wavefront-uniform)
+  auto flush = [&]() {
+    int off = 0;
+    while (off < used) {
+      const char* rec = ring + off;
+      const int meta = __builtin_amdgcn_readfirstlane(*(const int*)rec);
+      const int rs = meta & 0x7fffffff;
+      if (meta < 0) {
+        if (head_ok) {
+          const uint32_t* src = (const uint32_t*)(rec + 16) + li * 4 * kWordsFinal;
+          uint16_t* O = (uint16_t*)a.out + ((int64_t)rs * a.num_q_heads + h) * D;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            uint16_t* dst = O + kDL * (4 * g4 + i);
+            if constexpr (D == 128)
+              *(u32x4*)dst = *(const u32x4*)(src + 4 * i);
+            else
+              *(u32x2*)dst = *(const u32x2*)(src + 2 * i);
+          }
+        }
+        off += final_bytes;
+      } else {
+        if (head_ok) {
+          const f32x4* src = (const f32x4*)(rec + 16) + li * kDL;
+#pragma unroll
+          for (int d = 0; d < kDL; ++d) acc[d] = src[d];
+          const float2 ml = ((const float2*)(rec + 16 + 4 * G * 16 * kDL))[n];
+          store_partial<D, kBf16>(a, ((int64_t)rs + w) * a.num_q_heads + h, acc, ml.x, ml.y, g4);
+        }
+        off += part_bytes;
+      }
+    }
+    used = 0;
+  };
+  auto attend_next = [&](Tile<D>& t) -> bool {
+    attend_pair<D>(t, qb, acc, m, lsum, a.scale_log2, min(32, end_tok - 16 * ab), g4);
+    ab += 2;
+    if (ab < A.b1) return true;
+    float l = lsum;
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    if (pois_a) l = __builtin_nanf("");
+    {
+      // a record while it fits (G <= 16: at most 8,336 bytes), else a direct store
+      const int bytes = whole ? final_bytes : part_bytes;
+      if (used + bytes > ring_bytes) {
+        if (head_ok) {
+          const int64_t qo_row = ((int64_t)A.s * a.num_q_heads + h) * D;
+          if (whole)
+            store_final<D>((uint16_t*)a.out, qo_row, acc, l, g4);
+          else
+            store_partial<D, kBf16>(a, ((int64_t)A.s + w) * a.num_q_heads + h, acc, m, l, g4);
+        }
+      } else {
+        char* rec = ring + used;
+        if (lane == 0) *(int*)rec = A.s | (whole ? (int)0x80000000 : 0);
+        if (head_ok) {
+          if (whole) {
+            // the words store_final would write: row group i holds dims kDL (4 g4 + i) ..
+            const float inv = 1.f / l;
+            uint32_t* dst = (uint32_t*)(rec + 16) + li * 4 * kWordsFinal;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              if constexpr (D == 128) {
+                u32x4 wv;
+#pragma unroll
+                for (int t2 = 0; t2 < 4; ++t2) wv[t2] = pack_bf16x2(acc[2 * t2][i] * inv, acc[2 * t2 + 1][i] * inv);
+                *(u32x4*)(dst + 4 * i) = wv;
+              } else {
+                u32x2 wv;
+#pragma unroll
+                for (int t2 = 0; t2 < 2; ++t2) wv[t2] = pack_bf16x2(acc[2 * t2][i] * inv, acc[2 * t2 + 1][i] * inv);
+                *(u32x2*)(dst + 2 * i) = wv;
+              }
+            }
+          } else {
+            f32x4* dst = (f32x4*)(rec + 16) + li * kDL;
+#pragma unroll
+            for (int d = 0; d < kDL; ++d) dst[d] = acc[d];
+            if (g4 == 0) ((float2*)(rec + 16 + 4 * G * 16 * kDL))[n] = float2{m, l};
+          }
+        }
+        used += bytes;
+      }
+    }
+    if (A.end >= hi) return false;
+    const int pos = A.end;
+    A = span_from(A.s + 1, pos);
+    ab = A.b0;
+    end_tok = min(pool_keys<kAppend>(a, A.s), 16 * A.b1);
+    whole = !kAppend && !a.partial_only && pos == __builtin_amdgcn_readfirstlane(cum[A.s]) &&
+            A.end == __builtin_amdgcn_readfirstlane(cum[A.s + 1]);
+    pois_a = pois_next;
+    pois_next = false;
+    load_q(A.s);
+#pragma unroll
+    for (int t2 = 0; t2 < kDL; ++t2) acc[t2] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m = -INFINITY;
+    lsum = 0.f;
+    return true;
+  };
+
+  Tile<D> ta, tb;
+  issue_next(ta);
+  while (true) {
+    issue_next(tb);
+    if (!attend_next(ta)) break;
+    issue_next(ta);
+    if (!attend_next(tb)) break;
+  }
+  flush();
+}
+
+// Balanced mode: grid (W, kv-head groups); dynamic LDS holds S+1 ints and, but
+// for the lean kernel, each wavefront's staged results (kRingBytesPerWave).
 // kAppend: the pool is read up to each request's newest token and every segment
 // leaves a partial, which the merge combines with the newest key.
-// kLean: one wavefront per workgroup, segments through decode_segment_lean.
+// kLean: one wavefront per workgroup, segments through decode_segment_lean;
+// otherwise each wavefront streams its range through stream_range.
 template <int D, int NW, bool kAppend, bool kLean, bool kBf16 = false>
 __device__ __forceinline__ void balanced_body(const DecodeArgs& a) {
   extern __shared__ int32_t cum[];
@@ -546,31 +800,31 @@ __device__ __forceinline__ void balanced_body(const DecodeArgs& a) {
   // More attended blocks than the pool holds means blocks are shared (prefix
   // sharing): keep them cacheable. Otherwise stream K/V past the caches.
   const bool nt = a.nontemporal >= 0 ? a.nontemporal != 0 : T <= a.num_blocks;
-  int s = __builtin_amdgcn_readfirstlane(first);
-  int pos = lo;
-  while (pos < hi) {
-    const int cs = __builtin_amdgcn_readfirstlane(cum[s]);
-    const int ce = __builtin_amdgcn_readfirstlane(cum[s + 1]);
-    if (ce > pos) {
-      const int seg_end = min(ce, hi);
-      const int n_keys = pool_keys<kAppend>(a, s);
-      const bool whole = !kAppend && !a.partial_only && pos == cs && seg_end == ce;
-      const int64_t slot = (int64_t)s + w;
-      const int b0 = a.skip_blocks + pos - cs, b1 = a.skip_blocks + seg_end - cs;  // table indices
-      if constexpr (kLean) {
+  if constexpr (!kLean) {
+    if (nt)
+      stream_range<D, true, kAppend, kBf16>(a, cum, __builtin_amdgcn_readfirstlane(first), lo, hi, w, kvh);
+    else
+      stream_range<D, false, kAppend, kBf16>(a, cum, __builtin_amdgcn_readfirstlane(first), lo, hi, w, kvh);
+  } else {
+    int s = __builtin_amdgcn_readfirstlane(first);
+    int pos = lo;
+    while (pos < hi) {
+      const int cs = __builtin_amdgcn_readfirstlane(cum[s]);
+      const int ce = __builtin_amdgcn_readfirstlane(cum[s + 1]);
+      if (ce > pos) {
+        const int seg_end = min(ce, hi);
+        const int n_keys = pool_keys<kAppend>(a, s);
+        const bool whole = !kAppend && !a.partial_only && pos == cs && seg_end == ce;
+        const int64_t slot = (int64_t)s + w;
+        const int b0 = a.skip_blocks + pos - cs, b1 = a.skip_blocks + seg_end - cs;  // table indices
         if (nt)
           decode_segment_lean<D, true>(a, s, kvh, b0, b1, n_keys, whole, slot * a.num_q_heads, 1, q_lds);
         else
           decode_segment_lean<D, false>(a, s, kvh, b0, b1, n_keys, whole, slot * a.num_q_heads, 1, q_lds);
-      } else {
-        if (nt)
-          decode_segment<D, true, kBf16>(a, s, kvh, b0, b1, n_keys, whole, slot * a.num_q_heads, 1);
-        else
-          decode_segment<D, false, kBf16>(a, s, kvh, b0, b1, n_keys, whole, slot * a.num_q_heads, 1);
+        pos = seg_end;
       }
-      pos = seg_end;
+      ++s;
     }
-    ++s;
   }
 }
 
@@ -1099,6 +1353,31 @@ void launch_grid(const DecodeArgs& a, hipStream_t stream) {
                      dim3(64 * NW), 0, stream, a);
 }
 
+// The balanced kernel with a.ring_bytes set: LDS per wavefront for staged segment
+// results, from the compute unit's LDS shared by the workgroups that the
+// kernel's registers admit there, less the prefix sums (0: direct stores).
+template <int D, int NW, bool kAppend, bool kBf16>
+void launch_balanced(const DecodeArgs& args, hipStream_t stream) {
+  static const int64_t lds_per_wg = [] {
+    int dev = 0, lds = 65536, wgs = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess)
+      lds = 65536;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&wgs, decode_bf16_balanced_kernel<D, NW, kAppend, kBf16>,
+                                                      64 * NW, 0) != hipSuccess || wgs < 1)
+      wgs = 8;
+    (void)hipGetLastError();
+    return (int64_t)lds / wgs - 1024;  // slack for static LDS and allocation granules
+  }();
+  DecodeArgs a = args;
+  const int64_t per_wave = (lds_per_wg - (int64_t)ring_offset(a.num_seqs)) / NW;
+  a.ring_bytes = (int32_t)(std::max<int64_t>(0, std::min<int64_t>(kRingCapPerWave, per_wave)) & ~(int64_t)15);
+  const size_t lds = ring_offset(a.num_seqs) + (size_t)NW * a.ring_bytes;
+  const int groups = (a.num_kv_heads + NW - 1) / NW;
+  hipLaunchKernelGGL((decode_bf16_balanced_kernel<D, NW, kAppend, kBf16>), dim3(a.num_workers, groups),
+                     dim3(64 * NW), lds, stream, a);
+}
+
 template <int D, int NW>
 void launch_bf16_nw(const DecodeArgs& a, hipStream_t stream) {
   if (a.num_workers > 0 && a.lean) {
@@ -1110,17 +1389,12 @@ void launch_bf16_nw(const DecodeArgs& a, hipStream_t stream) {
       hipLaunchKernelGGL((decode_bf16_lean_kernel<D, false>), dim3(a.num_workers, a.num_kv_heads), dim3(64),
                          lds, stream, a);
   } else if (a.num_workers > 0) {
-    const int groups = (a.num_kv_heads + NW - 1) / NW;
-    const size_t lds = sizeof(int32_t) * (size_t)(a.num_seqs + 1);
     if (a.new_k != nullptr)
-      hipLaunchKernelGGL((decode_bf16_balanced_kernel<D, NW, true>), dim3(a.num_workers, groups),
-                         dim3(64 * NW), lds, stream, a);
+      launch_balanced<D, NW, true, false>(a, stream);
     else if (a.partial_only)  // shared-prefix mode: bf16 partials
-      hipLaunchKernelGGL((decode_bf16_balanced_kernel<D, NW, false, true>), dim3(a.num_workers, groups),
-                         dim3(64 * NW), lds, stream, a);
+      launch_balanced<D, NW, false, true>(a, stream);
     else
-      hipLaunchKernelGGL((decode_bf16_balanced_kernel<D, NW, false>), dim3(a.num_workers, groups),
-                         dim3(64 * NW), lds, stream, a);
+      launch_balanced<D, NW, false, false>(a, stream);
   } else if (a.nontemporal > 0) {
     launch_grid<D, NW, true>(a, stream);
   } else {

@@ -99,6 +99,8 @@ struct DecodeArgs {
   int32_t* split_req;
   int32_t merge_splits;      // balanced merge grid runs over split_req instead of requests
   int32_t lean;              // balanced mode: the lean decode kernel (one wavefront per workgroup)
+  int32_t ring_bytes;        // balanced mode: LDS bytes per wavefront for staged segment results
+                             // (set at launch; 0 = each segment stores its result directly)
   float scale_log2;  // scale * log2(e)
   // Append mode (balanced bf16 only; both null otherwise): [S][Hkv][D] K and V of
   // each request's newest token, position context_len - 1. The decode kernel

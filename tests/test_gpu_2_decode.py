@@ -297,6 +297,20 @@ def test_append_bad_length_and_block(part):
     assert_close(o[good], ref[good], "bf16", "append, requests next to bad ones")
 
 
+@pytest.mark.parametrize("group", [4, 16])
+def test_staged_results_overflow(group, monkeypatch):
+    """Sixteen workers over 400 short requests: about 25 segments per wavefront, more than
+    its LDS holds (G=4: 14 whole-request results or 7 partials; G=16: 3 or 1), so results
+    are staged until the buffer is full and stored directly after that. Plain decode (whole
+    requests) and decode-append (partials), against the oracle."""
+    say(f"  decode of 400 short requests over 16 workers, G={group}")
+    monkeypatch.setenv("PA_DECODE_WORKERS", "16")
+    lens = np.random.default_rng(40 + group).integers(1, 49, 400).tolist()
+    w = workloads.custom_decode(400 + group, lens, Hq=8 * group, Hkv=8, D=128, dtype="bf16")
+    check(w, 0, f"staged results G={group}")
+    check_append(w, 0, f"append, staged results G={group}")
+
+
 @pytest.mark.parametrize("S", [8192, 8193])
 def test_batch_size_limit(S):
     """The largest batch the balanced split takes (its block prefix sums fill LDS) and one more

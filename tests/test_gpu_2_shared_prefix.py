@@ -74,6 +74,15 @@ def test_many_requests_and_key_ranges():
     check(w, 64, "600 requests")
 
 
+def test_tail_results_overflow(monkeypatch):
+    """Sixteen workers over the tails of 300 requests: about 19 tail segments per wavefront,
+    more bf16 partials than its LDS holds (7 at G=4), so the rest are stored directly."""
+    say("  shared-prefix decode, 300 requests over 16 workers")
+    monkeypatch.setenv("PA_DECODE_WORKERS", "16")
+    w = workloads.c3_prefix_shared(seed=81, num_seqs=300)
+    check(w, w.shared_prefix_tokens // 16, "300 requests, 16 workers")
+
+
 def test_few_requests_long_prefix():
     """Two requests behind an 8,192-token prefix: the prefix is split into many key ranges."""
     w = workloads.custom_decode(79, [8200, 8500], Hq=32, Hkv=8, D=128, dtype="bf16", shared_prefix_tokens=8192)
