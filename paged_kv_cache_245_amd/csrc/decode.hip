@@ -478,7 +478,7 @@ __device__ __forceinline__ int request_blocks(const DecodeArgs& a, int s) {
 // operations retire in order, so a store holds up every later wait on a load
 // until the store is acknowledged; under a full read stream that costs several
 // microseconds per store, once per segment. Staged, the stores all go out after
-// the last load is used. Each wavefront has kRingBytesPerWave of LDS, filled
+// the last load is used. Each wavefront has a.ring_bytes of LDS, filled
 // front to back with records: a 16-byte header (request; top bit set for a
 // whole request), then for a whole request the final bf16 words of its 4 G
 // lanes (what store_final writes), else their fp32 acc followed by (m, l) per
@@ -599,8 +599,6 @@ __device__ __forceinline__ void stream_range(const DecodeArgs& a, const int32_t*
       }
     }
   };
-  // attend the pair at the attend cursor; at the end of segment A, store it and
-  // move A on (returns false after the worker's last segment)
   // this wavefront's records, after the prefix sums; written out after the last segment
   constexpr int kWordsFinal = D / 32;             // u32 words per (lane, row group i) of a final
   const int li = n * 4 + g4;                      // record row of this lane (n < G)
@@ -642,6 +640,8 @@ __device__ __forceinline__ void stream_range(const DecodeArgs& a, const int32_t*
     }
     used = 0;
   };
+  // attend the pair at the attend cursor; at the end of segment A, record (or store)
+  // its result and move A on (returns false after the worker's last segment)
   auto attend_next = [&](Tile<D>& t) -> bool {
     attend_pair<D>(t, qb, acc, m, lsum, a.scale_log2, min(32, end_tok - 16 * ab), g4);
     ab += 2;
@@ -722,7 +722,7 @@ __device__ __forceinline__ void stream_range(const DecodeArgs& a, const int32_t*
 }
 
 // Balanced mode: grid (W, kv-head groups); dynamic LDS holds S+1 ints and, but
-// for the lean kernel, each wavefront's staged results (kRingBytesPerWave).
+// for the lean kernel, each wavefront's staged results (a.ring_bytes).
 // kAppend: the pool is read up to each request's newest token and every segment
 // leaves a partial, which the merge combines with the newest key.
 // kLean: one wavefront per workgroup, segments through decode_segment_lean;
