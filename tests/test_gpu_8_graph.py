@@ -183,3 +183,17 @@ def test_shared_prefix_call_replayed_matches_eager():
         torch.cuda.synchronize()
     ok, ov = oracle_pools(w)
     assert_close(as64(out_g), oracle_decode(w, ok, ov), "bf16", "shared prefix, graph-replayed")
+
+
+def test_first_decode_call_inside_capture():
+    """In a fresh process, the library's first decode call (pa_decode_append_noalloc) is made
+    inside a graph capture, so its one-time set-up runs during the capture; replays must equal
+    eager pa_decode_append bit for bit (tests/graph_first_call.py, run as a child process)."""
+    import os
+    import subprocess
+    import sys
+    say("  first decode call inside a graph capture (child process)")
+    here = os.path.dirname(os.path.abspath(__file__))
+    r = subprocess.run([sys.executable, "-u", os.path.join(here, "graph_first_call.py")], capture_output=True,
+                       text=True, timeout=300)
+    assert r.returncode == 0 and "first-call capture ok" in r.stdout, (r.stdout[-2000:], r.stderr[-2000:])
