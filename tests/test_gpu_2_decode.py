@@ -186,6 +186,19 @@ def test_balanced_worker_counts(workers, monkeypatch):
     check(w, 0, f"workers {workers}")
 
 
+@pytest.mark.parametrize("workers", [None, 1000])
+def test_one_long_request_many_partials(workers, monkeypatch):
+    """One request of 32,768 tokens split over every worker: 256 partials per (request, q head)
+    with the default worker count (one round of the wide merge), 1,000 with 1,000 workers
+    (several rounds). pa_decode and pa_decode_append against the oracle."""
+    say(f"  one 32,768-token request, workers {workers or 'default'}")
+    if workers:
+        monkeypatch.setenv("PA_DECODE_WORKERS", str(workers))
+    w = workloads.custom_decode(57, [32768], Hq=32, Hkv=8, D=128, dtype="bf16")
+    check(w, 0, f"one long request, workers {workers}")
+    check_append(w, 0, f"append, one long request, workers {workers}")
+
+
 @pytest.mark.parametrize("nt", ["0", "1"])
 def test_load_flavours(nt, monkeypatch):
     monkeypatch.setenv("PA_DECODE_NT", nt)
