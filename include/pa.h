@@ -186,6 +186,37 @@ int pa_prefill_chunk_append(const pa_cache_desc* desc, void* out, const void* q,
                             int32_t num_seqs, int32_t num_tokens, int32_t max_query_len, int32_t max_seq_len,
                             float scale, void* stream);
 
+/* pa_prefill_chunk for steps whose chunks are a few tokens long (a request
+ * that scores several tokens at once, as speculative decoding does, or the last
+ * rows of a prompt): the same result, computed the way pa_decode computes one
+ * token. The KV cache of a request is read once per kv head for all its chunk
+ * rows (the reads of past K/V dominate such a step: arcyou teardown, "The
+ * problem both ideas solve"), split evenly over the device's workgroups by
+ * blocks as pa_decode's balanced mode splits them, and a second kernel merges
+ * the partial softmaxes of rows whose keys were split. Row i of request s's
+ * chunk of n_s rows sits at position seq_lens[s] - n_s + i and attends keys 0 ..
+ * that position, as in pa_prefill_chunk; the chunk's K/V must already be in the
+ * pool. PA_BF16 only.
+ *   max_query_len  at most pa_prefill_chunk_short_max_query_len(desc) =
+ *                  16 / (num_q_heads / num_kv_heads): rows times q heads per kv
+ *                  head fill at most the 16 columns of the kernel's score tile
+ *   num_seqs       at most 8192
+ *   workspace      device scratch of at least
+ *                  pa_prefill_chunk_short_workspace_size(desc, num_seqs,
+ *                  max_query_len) bytes; contents on entry do not matter;
+ *                  concurrent calls need separate workspaces
+ * All other arguments are those of pa_prefill_chunk. Errors: those of
+ * pa_prefill_chunk; PA_ERR_UNSUPPORTED past the limits above; PA_ERR_WORKSPACE
+ * for a missing or short workspace. */
+int32_t pa_prefill_chunk_short_max_query_len(const pa_cache_desc* desc);
+size_t pa_prefill_chunk_short_workspace_size(const pa_cache_desc* desc, int32_t num_seqs,
+                                             int32_t max_query_len);
+int pa_prefill_chunk_short(const pa_cache_desc* desc, void* out, const void* q, const void* k_cache,
+                           const void* v_cache, const int32_t* query_start_loc, const int32_t* seq_lens,
+                           const int32_t* block_tables, int32_t max_blocks_per_seq, int32_t num_seqs,
+                           int32_t num_tokens, int32_t max_query_len, int32_t max_seq_len, float scale,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
 /* Decode after appending each request's newest token: the same result as
  * pa_write_kv of those tokens into their slots followed by pa_decode. Where the
  * decode runs in its balanced bf16 mode (the default for bf16 pools,

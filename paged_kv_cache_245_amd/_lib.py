@@ -22,7 +22,8 @@ BLOCK_SIZE = 16
 EXPORTED = ("pa_write_kv", "pa_decode_partition_tokens", "pa_decode_workspace_size", "pa_decode",
             "pa_decode_append", "pa_decode_append_lean", "pa_decode_append_noalloc",
             "pa_decode_shared_prefix_workspace_size", "pa_decode_shared_prefix",
-            "pa_prefill_chunk", "pa_prefill_chunk_append", "pa_copy_blocks", "pa_swap_blocks", "pa_gather_kv", "pa_strerror", "pa_last_error_detail",
+            "pa_prefill_chunk", "pa_prefill_chunk_append", "pa_prefill_chunk_short_max_query_len",
+            "pa_prefill_chunk_short_workspace_size", "pa_prefill_chunk_short", "pa_copy_blocks", "pa_swap_blocks", "pa_gather_kv", "pa_strerror", "pa_last_error_detail",
             "pa_version", "pa_bench_copy", "pa_bench_read", "pa_bench_flush", "pa_bench_mfma")
 
 
@@ -76,6 +77,9 @@ def load():
         "pa_decode_shared_prefix": (ctypes.c_int, [D, P, P, P, P, P, I32, P, I32, I32, I32, F, P, SZ, P]),
         "pa_prefill_chunk": (ctypes.c_int, [D, P, P, P, P, P, P, P, I32, I32, I32, I32, I32, F, P]),
         "pa_prefill_chunk_append": (ctypes.c_int, [D, P, P, P, P, P, P, P, P, P, I32, I32, I32, I32, I32, F, P]),
+        "pa_prefill_chunk_short_max_query_len": (I32, [D]),
+        "pa_prefill_chunk_short_workspace_size": (SZ, [D, I32, I32]),
+        "pa_prefill_chunk_short": (ctypes.c_int, [D, P, P, P, P, P, P, P, I32, I32, I32, I32, I32, F, P, SZ, P]),
         "pa_copy_blocks": (ctypes.c_int, [D, P, P, P, I64, P]),
         "pa_swap_blocks": (ctypes.c_int, [D, P, P, P, P, I64, P, I64, I32, P]),
         "pa_gather_kv": (ctypes.c_int, [D, P, P, P, P, P, I32, P, I32, I32, P]),
@@ -367,6 +371,47 @@ def pa_prefill_chunk_append(desc, out, q, key, value, k_cache, v_cache, query_st
                                         _ptr(block_tables), block_tables.shape[1], S, q.shape[0],
                                         int(max_query_len), int(max_seq_len), float(scale), _stream(stream, q))
     _check(st, "pa_prefill_chunk_append")
+
+
+def pa_prefill_chunk_short_max_query_len(desc) -> int:
+    st = load().pa_prefill_chunk_short_max_query_len(ctypes.byref(desc))
+    _check(min(st, 0), "pa_prefill_chunk_short_max_query_len")
+    return st
+
+
+def pa_prefill_chunk_short_workspace_size(desc, num_seqs, max_query_len) -> int:
+    return load().pa_prefill_chunk_short_workspace_size(ctypes.byref(desc), num_seqs, max_query_len)
+
+
+def chunk_short_workspace(desc, num_seqs, max_query_len, device="cuda"):
+    """A device workspace tensor (uint8) of the size pa_prefill_chunk_short needs, or None."""
+    n = pa_prefill_chunk_short_workspace_size(desc, num_seqs, max_query_len)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
+def pa_prefill_chunk_short(desc, out, q, k_cache, v_cache, query_start_loc, seq_lens, block_tables,
+                           max_query_len, max_seq_len, scale, workspace, stream=None):
+    """pa_prefill_chunk for chunks of at most 16 / (Hq / Hkv) rows, through the decode kernel;
+    workspace from chunk_short_workspace."""
+    dt = torch_dtype(desc)
+    for t, n in ((out, "out"), (q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _need(t, dt, n)
+    for t, n in ((query_start_loc, "query_start_loc"), (seq_lens, "seq_lens")):
+        _need(t, torch.int32, n, 1)
+    _need(block_tables, torch.int32, "block_tables", 2)
+    S = seq_lens.numel()
+    _pools(desc, k_cache, v_cache)
+    _rows(q, "q", 0, desc.num_q_heads, desc.head_dim)
+    _rows(out, "out", q.shape[0], desc.num_q_heads, desc.head_dim)
+    _shape(query_start_loc, "query_start_loc", S + 1)
+    _table_rows(block_tables, S)
+    ws_bytes = _nbytes(workspace) if workspace is not None else 0
+    st = load().pa_prefill_chunk_short(ctypes.byref(desc), _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                       _ptr(query_start_loc), _ptr(seq_lens), _ptr(block_tables),
+                                       block_tables.shape[1], S, q.shape[0], int(max_query_len),
+                                       int(max_seq_len), float(scale), _ptr(workspace), ws_bytes,
+                                       _stream(stream, q))
+    _check(st, "pa_prefill_chunk_short")
 
 
 def pa_copy_blocks(desc, k_cache, v_cache, block_pairs, stream=None):

@@ -126,10 +126,14 @@ __device__ __forceinline__ void load_pair(Tile<D>& t, const uint16_t* K, const u
 }
 
 // Online-softmax update with one pair of blocks; `valid` = keys of the pair
-// (0..32, in order) that belong to the range being attended.
-template <int D>
+// (0..32, in order) that belong to the range being attended. kCols (short-chunk
+// mode): this lane's column also masks the keys from col_valid on (its position's
+// causal limit), and a column that has seen no key yet keeps m = -inf, l = 0 and
+// acc = 0 (the max is taken as 0 in the exponentials while it is -inf).
+template <int D, bool kCols = false>
 __device__ __forceinline__ void attend_pair(Tile<D>& t, const u32x4* qb, f32x4* acc, float& m,
-                                            float& lsum, float scale_log2, int valid, int g4) {
+                                            float& lsum, float scale_log2, int valid, int g4,
+                                            int col_valid = 32) {
   constexpr int kDL = D / 16;
   typedef typename VRowT<D>::type VRow;
   f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
@@ -153,18 +157,26 @@ __device__ __forceinline__ void attend_pair(Tile<D>& t, const u32x4* qb, f32x4* 
       }
     }
   }
+  if constexpr (kCols) {
+    if (col_valid < 32) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if ((j >> 2) * 16 + 4 * g4 + (j & 3) >= col_valid) sc[j] = -INFINITY;
+    }
+  }
   float tmax = sc[0];
 #pragma unroll
   for (int j = 1; j < 8; ++j) tmax = fmaxf(tmax, sc[j]);
   tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
   tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
   const float m_new = fmaxf(m, tmax);
-  const float alpha = fast_exp2(m - m_new);
+  const float m_use = (kCols && m_new == -INFINITY) ? 0.f : m_new;
+  const float alpha = fast_exp2(m - m_use);
   float p[8];
   float psum = 0.f;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    p[j] = fast_exp2(sc[j] - m_new);
+    p[j] = fast_exp2(sc[j] - m_use);
     psum += p[j];
   }
   lsum = lsum * alpha + psum;
@@ -496,7 +508,9 @@ __host__ __device__ constexpr size_t ring_offset(int S) { return ((size_t)(S + 1
 // one pair ahead of the attend cursor, so it is in the attended segment or the
 // one after it; the block ids of the segment after the issue cursor's are
 // fetched when the cursor enters a segment.
-template <int D, bool kNT, bool kAppend, bool kBf16>
+// kCols: short-chunk mode (see DecodeArgs); lane column n is position n / G, q head
+// n % G, the C = n_cols * G columns in use.
+template <int D, bool kNT, bool kAppend, bool kBf16, bool kCols = false>
 __device__ __forceinline__ void stream_range(const DecodeArgs& a, const int32_t* cum, int first, int lo,
                                              int hi, int w, int kvh) {
   constexpr int kChunks = D / 32;
@@ -505,9 +519,21 @@ __device__ __forceinline__ void stream_range(const DecodeArgs& a, const int32_t*
   const int n = lane & 15;
   const int g4 = lane >> 4;
   const int G = a.group;
+  const int C = kCols ? a.n_cols * G : G;      // columns in use
+  const int pc = kCols ? n / G : 0;            // this lane's position (short-chunk mode)
   const int Hkv = a.num_kv_heads;
-  const int h = kvh * G + n;
-  const bool head_ok = n < G;
+  const int h = kvh * G + (kCols ? n % G : n);
+  const bool lane_ok = n < C;
+  // rows of request s in short-chunk mode: [query_start_loc[s], query_start_loc[s + 1])
+  auto chunk_of = [&](int s, int& q0, int& nq) {
+    q0 = kCols ? a.query_start_loc[s] : s;
+    nq = kCols ? a.query_start_loc[s + 1] - q0 : 1;
+  };
+  // output row (the q row) and partial row of (request s, this lane's column)
+  auto out_row = [&](int s, int q0) -> int64_t { return ((int64_t)(kCols ? q0 + pc : s) * a.num_q_heads + h) * D; };
+  auto part_row = [&](int s) -> int64_t {
+    return kCols ? (((int64_t)s + w) * a.n_cols + pc) * a.num_q_heads + h : ((int64_t)s + w) * a.num_q_heads + h;
+  };
   const uint16_t* __restrict__ K = (const uint16_t*)a.k;
   const uint16_t* __restrict__ V = (const uint16_t*)a.v;
   const LaneOffsets offs = lane_offsets<D>(kvh, Hkv, n, g4);
@@ -549,15 +575,21 @@ __device__ __forceinline__ void stream_range(const DecodeArgs& a, const int32_t*
     idv_n = ids_of(N, N.b0);
   }
   bool pois_a = false, pois_next = false;
+  // segment A's chunk (short-chunk mode): its first q row and row count, whether this
+  // lane's column is one of its positions, and that position's causal limit
+  int q0A, nqA;
+  chunk_of(A.s, q0A, nqA);
+  bool col_ok = lane_ok && (!kCols || pc < nqA);
+  int col_lim = kCols ? pool_keys<kAppend>(a, A.s) - nqA + pc + 1 : 0;
 
   u32x4 qb[kChunks];
-  auto load_q = [&](int s) {
-    const int64_t qo_row = ((int64_t)s * a.num_q_heads + h) * D;
+  auto load_q = [&](int s, int q0) {
+    const int64_t qo_row = out_row(s, q0);
 #pragma unroll
     for (int c = 0; c < kChunks; ++c)
-      qb[c] = head_ok ? *(const u32x4*)((const uint16_t*)a.q + qo_row + 32 * c + 8 * g4) : u32x4{0, 0, 0, 0};
+      qb[c] = col_ok ? *(const u32x4*)((const uint16_t*)a.q + qo_row + 32 * c + 8 * g4) : u32x4{0, 0, 0, 0};
   };
-  load_q(A.s);
+  load_q(A.s, q0A);
   f32x4 acc[kDL];
 #pragma unroll
   for (int t = 0; t < kDL; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -601,9 +633,9 @@ __device__ __forceinline__ void stream_range(const DecodeArgs& a, const int32_t*
   };
   // this wavefront's records, after the prefix sums; written out after the last segment
   constexpr int kWordsFinal = D / 32;             // u32 words per (lane, row group i) of a final
-  const int li = n * 4 + g4;                      // record row of this lane (n < G)
-  const int final_bytes = 16 + 4 * G * (4 * kWordsFinal * 4);
-  const int part_bytes = (16 + 4 * G * (16 * kDL) + 8 * G + 15) & ~15;  // records stay 16-byte aligned
+  const int li = n * 4 + g4;                      // record row of this lane (n < C)
+  const int final_bytes = 16 + 4 * C * (4 * kWordsFinal * 4);
+  const int part_bytes = (16 + 4 * C * (16 * kDL) + 8 * C + 15) & ~15;  // records stay 16-byte aligned
   const int ring_bytes = a.ring_bytes;
   char* ring = (char*)cum + ring_offset(a.num_seqs) + (size_t)(threadIdx.x >> 6) * ring_bytes;
   int used = 0;  // bytes of records (wavefront-uniform)
@@ -613,10 +645,16 @@ __device__ __forceinline__ void stream_range(const DecodeArgs& a, const int32_t*
       const char* rec = ring + off;
       const int meta = __builtin_amdgcn_readfirstlane(*(const int*)rec);
       const int rs = meta & 0x7fffffff;
+      int rq0 = rs, rnq = 1;  // the chunk's first q row and row count (short-chunk mode)
+      if constexpr (kCols) {
+        rq0 = __builtin_amdgcn_readfirstlane(((const int*)rec)[1]);
+        rnq = __builtin_amdgcn_readfirstlane(((const int*)rec)[2]);
+      }
+      const bool rok = lane_ok && (!kCols || pc < rnq);
       if (meta < 0) {
-        if (head_ok) {
+        if (rok) {
           const uint32_t* src = (const uint32_t*)(rec + 16) + li * 4 * kWordsFinal;
-          uint16_t* O = (uint16_t*)a.out + ((int64_t)rs * a.num_q_heads + h) * D;
+          uint16_t* O = (uint16_t*)a.out + out_row(rs, rq0);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             uint16_t* dst = O + kDL * (4 * g4 + i);
@@ -628,12 +666,12 @@ __device__ __forceinline__ void stream_range(const DecodeArgs& a, const int32_t*
         }
         off += final_bytes;
       } else {
-        if (head_ok) {
+        if (rok) {
           const f32x4* src = (const f32x4*)(rec + 16) + li * kDL;
 #pragma unroll
           for (int d = 0; d < kDL; ++d) acc[d] = src[d];
-          const float2 ml = ((const float2*)(rec + 16 + 4 * G * 16 * kDL))[n];
-          store_partial<D, kBf16>(a, ((int64_t)rs + w) * a.num_q_heads + h, acc, ml.x, ml.y, g4);
+          const float2 ml = ((const float2*)(rec + 16 + 4 * C * 16 * kDL))[n];
+          store_partial<D, kBf16>(a, part_row(rs), acc, ml.x, ml.y, g4);
         }
         off += part_bytes;
       }
@@ -643,7 +681,7 @@ __device__ __forceinline__ void stream_range(const DecodeArgs& a, const int32_t*
   // attend the pair at the attend cursor; at the end of segment A, record (or store)
   // its result and move A on (returns false after the worker's last segment)
   auto attend_next = [&](Tile<D>& t) -> bool {
-    attend_pair<D>(t, qb, acc, m, lsum, a.scale_log2, min(32, end_tok - 16 * ab), g4);
+    attend_pair<D, kCols>(t, qb, acc, m, lsum, a.scale_log2, min(32, end_tok - 16 * ab), g4, col_lim - 16 * ab);
     ab += 2;
     if (ab < A.b1) return true;
     float l = lsum;
@@ -651,20 +689,25 @@ __device__ __forceinline__ void stream_range(const DecodeArgs& a, const int32_t*
     l += __shfl_xor(l, 32, 64);
     if (pois_a) l = __builtin_nanf("");
     {
-      // a record while it fits (G <= 16: at most 8,336 bytes), else a direct store
+      // a record while it fits (C <= 16 columns: at most 8,336 bytes), else a direct store
       const int bytes = whole ? final_bytes : part_bytes;
       if (used + bytes > ring_bytes) {
-        if (head_ok) {
-          const int64_t qo_row = ((int64_t)A.s * a.num_q_heads + h) * D;
+        if (col_ok) {
           if (whole)
-            store_final<D>((uint16_t*)a.out, qo_row, acc, l, g4);
+            store_final<D>((uint16_t*)a.out, out_row(A.s, q0A), acc, l, g4);
           else
-            store_partial<D, kBf16>(a, ((int64_t)A.s + w) * a.num_q_heads + h, acc, m, l, g4);
+            store_partial<D, kBf16>(a, part_row(A.s), acc, m, l, g4);
         }
       } else {
         char* rec = ring + used;
-        if (lane == 0) *(int*)rec = A.s | (whole ? (int)0x80000000 : 0);
-        if (head_ok) {
+        if (lane == 0) {
+          ((int*)rec)[0] = A.s | (whole ? (int)0x80000000 : 0);
+          if constexpr (kCols) {
+            ((int*)rec)[1] = q0A;
+            ((int*)rec)[2] = nqA;
+          }
+        }
+        if (col_ok) {
           if (whole) {
             // the words store_final would write: row group i holds dims kDL (4 g4 + i) ..
             const float inv = 1.f / l;
@@ -687,7 +730,7 @@ __device__ __forceinline__ void stream_range(const DecodeArgs& a, const int32_t*
             f32x4* dst = (f32x4*)(rec + 16) + li * kDL;
 #pragma unroll
             for (int d = 0; d < kDL; ++d) dst[d] = acc[d];
-            if (g4 == 0) ((float2*)(rec + 16 + 4 * G * 16 * kDL))[n] = float2{m, l};
+            if (g4 == 0) ((float2*)(rec + 16 + 4 * C * 16 * kDL))[n] = float2{m, l};
           }
         }
         used += bytes;
@@ -702,7 +745,12 @@ __device__ __forceinline__ void stream_range(const DecodeArgs& a, const int32_t*
             A.end == __builtin_amdgcn_readfirstlane(cum[A.s + 1]);
     pois_a = pois_next;
     pois_next = false;
-    load_q(A.s);
+    if constexpr (kCols) {
+      chunk_of(A.s, q0A, nqA);
+      col_ok = lane_ok && pc < nqA;
+      col_lim = pool_keys<kAppend>(a, A.s) - nqA + pc + 1;
+    }
+    load_q(A.s, q0A);
 #pragma unroll
     for (int t2 = 0; t2 < kDL; ++t2) acc[t2] = f32x4{0.f, 0.f, 0.f, 0.f};
     m = -INFINITY;
@@ -727,7 +775,8 @@ __device__ __forceinline__ void stream_range(const DecodeArgs& a, const int32_t*
 // leaves a partial, which the merge combines with the newest key.
 // kLean: one wavefront per workgroup, segments through decode_segment_lean;
 // otherwise each wavefront streams its range through stream_range.
-template <int D, int NW, bool kAppend, bool kLean, bool kBf16 = false>
+// kCols: short-chunk mode (see DecodeArgs).
+template <int D, int NW, bool kAppend, bool kLean, bool kBf16 = false, bool kCols = false>
 __device__ __forceinline__ void balanced_body(const DecodeArgs& a) {
   extern __shared__ int32_t cum[];
   __shared__ u32x4 q_lds[kLean ? (D / 32) * 64 : 1];  // the lean segments' query operands
@@ -802,9 +851,9 @@ __device__ __forceinline__ void balanced_body(const DecodeArgs& a) {
   const bool nt = a.nontemporal >= 0 ? a.nontemporal != 0 : T <= a.num_blocks;
   if constexpr (!kLean) {
     if (nt)
-      stream_range<D, true, kAppend, kBf16>(a, cum, __builtin_amdgcn_readfirstlane(first), lo, hi, w, kvh);
+      stream_range<D, true, kAppend, kBf16, kCols>(a, cum, __builtin_amdgcn_readfirstlane(first), lo, hi, w, kvh);
     else
-      stream_range<D, false, kAppend, kBf16>(a, cum, __builtin_amdgcn_readfirstlane(first), lo, hi, w, kvh);
+      stream_range<D, false, kAppend, kBf16, kCols>(a, cum, __builtin_amdgcn_readfirstlane(first), lo, hi, w, kvh);
   } else {
     int s = __builtin_amdgcn_readfirstlane(first);
     int pos = lo;
@@ -831,6 +880,13 @@ __device__ __forceinline__ void balanced_body(const DecodeArgs& a) {
 template <int D, int NW, bool kAppend, bool kBf16 = false>
 __global__ __launch_bounds__(64 * NW) void decode_bf16_balanced_kernel(DecodeArgs a) {
   balanced_body<D, NW, kAppend, false, kBf16>(a);
+}
+
+// Short-chunk mode: the balanced decode with the columns of a kv head's score tile
+// spread over the chunk's positions (pa_prefill_chunk_short).
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) void decode_bf16_chunk_kernel(DecodeArgs a) {
+  balanced_body<D, NW, false, false, false, true>(a);
 }
 
 // The lean decode: grid (W, kv heads), one wavefront each, within 96 registers so
@@ -1003,6 +1059,41 @@ __global__ __launch_bounds__(64 * kMergeHeads) void decode_merge_balanced_kernel
   }
   if (L <= 0) den = __builtin_nanf("");  // no key (in append mode, no newest token): NaN
   const float inv = 1.f / den;
+  if constexpr (kE == 2)
+    *(uint32_t*)(O + orow) = pack_bf16x2(o[0] * inv, o[1] * inv);
+  else
+    O[orow] = f32_to_bf16_bits(o[0] * inv);
+}
+
+// Short-chunk mode merge, one wavefront per (q head, request, position): the
+// partials of (request s, position p, head h) are rows ((s + w) n_cols + p) Hq + h
+// for the workers w0 .. w1 that read its blocks; a request read by one worker
+// was written by the decode kernel. Every position attends key 0, which the
+// first partial holds, so the fold's first batch has a finite maximum.
+template <int D>
+__global__ __launch_bounds__(64 * kMergeHeads) void decode_merge_chunk_kernel(DecodeArgs a) {
+  constexpr int kE = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int h = blockIdx.y * kMergeHeads + (threadIdx.x >> 6);
+  if (h >= a.num_q_heads) return;  // whole wavefront; the kernel has no barrier
+  const int s = blockIdx.x / a.n_cols, p = blockIdx.x % a.n_cols;  // grid x: (request, position)
+  const int q0 = a.query_start_loc[s], nq = a.query_start_loc[s + 1] - q0;
+  const int L = min(a.context_lens[s], a.max_context_len);
+  const int64_t T = a.cum_blocks[a.num_seqs];
+  const int64_t c0 = a.cum_blocks[s], c1 = a.cum_blocks[s + 1];
+  if (p >= nq || L <= 0) return;  // no such position (a chunk with rows has keys)
+  const int64_t Tn = max(T, (int64_t)1);
+  const int W = (int)min((int64_t)a.num_workers, Tn);  // as in the decode kernel
+  const int w0 = worker_of(c0, Tn, W);
+  const int w1 = worker_of(max(c1 - 1, c0), Tn, W);
+  if (w0 == w1) return;  // one segment: written by the decode kernel
+  const int64_t rstep = (int64_t)a.n_cols * a.num_q_heads;
+  const int64_t row0 = ((int64_t)s + w0) * rstep + (int64_t)p * a.num_q_heads + h;
+  float o[kE], den, M;
+  fold_partials<D>(a.part_acc, a.part_ml, row0, rstep, w1 - w0 + 1, lane, o, den, M);
+  const float inv = 1.f / den;
+  uint16_t* O = (uint16_t*)a.out;
+  const int64_t orow = ((int64_t)(q0 + p) * a.num_q_heads + h) * D + kE * lane;
   if constexpr (kE == 2)
     *(uint32_t*)(O + orow) = pack_bf16x2(o[0] * inv, o[1] * inv);
   else
@@ -1356,15 +1447,16 @@ void launch_grid(const DecodeArgs& a, hipStream_t stream) {
 // The balanced kernel with a.ring_bytes set: LDS per wavefront for staged segment
 // results, from the compute unit's LDS shared by the workgroups that the
 // kernel's registers admit there, less the prefix sums (0: direct stores).
-template <int D, int NW, bool kAppend, bool kBf16>
+// kCols: the short-chunk kernel instead.
+template <int D, int NW, bool kAppend, bool kBf16, bool kCols = false>
 void launch_balanced(const DecodeArgs& args, hipStream_t stream) {
+  constexpr auto kernel = kCols ? decode_bf16_chunk_kernel<D, NW> : decode_bf16_balanced_kernel<D, NW, kAppend, kBf16>;
   static const int64_t lds_per_wg = [] {
     int dev = 0, lds = 65536, wgs = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess)
       lds = 65536;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&wgs, decode_bf16_balanced_kernel<D, NW, kAppend, kBf16>,
-                                                      64 * NW, 0) != hipSuccess || wgs < 1)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&wgs, kernel, 64 * NW, 0) != hipSuccess || wgs < 1)
       wgs = 8;
     (void)hipGetLastError();
     return (int64_t)lds / wgs - 1024;  // slack for static LDS and allocation granules
@@ -1374,13 +1466,14 @@ void launch_balanced(const DecodeArgs& args, hipStream_t stream) {
   a.ring_bytes = (int32_t)(std::max<int64_t>(0, std::min<int64_t>(kRingCapPerWave, per_wave)) & ~(int64_t)15);
   const size_t lds = ring_offset(a.num_seqs) + (size_t)NW * a.ring_bytes;
   const int groups = (a.num_kv_heads + NW - 1) / NW;
-  hipLaunchKernelGGL((decode_bf16_balanced_kernel<D, NW, kAppend, kBf16>), dim3(a.num_workers, groups),
-                     dim3(64 * NW), lds, stream, a);
+  hipLaunchKernelGGL(kernel, dim3(a.num_workers, groups), dim3(64 * NW), lds, stream, a);
 }
 
 template <int D, int NW>
 void launch_bf16_nw(const DecodeArgs& a, hipStream_t stream) {
-  if (a.num_workers > 0 && a.lean) {
+  if (a.query_start_loc != nullptr) {
+    launch_balanced<D, NW, false, false, true>(a, stream);
+  } else if (a.num_workers > 0 && a.lean) {
     const size_t lds = sizeof(int32_t) * (size_t)(a.num_seqs + 1);
     if (a.new_k != nullptr)
       hipLaunchKernelGGL((decode_bf16_lean_kernel<D, true>), dim3(a.num_workers, a.num_kv_heads), dim3(64),
@@ -1409,7 +1502,7 @@ hipError_t launch_decode_d(const DecodeArgs& args, bool bf16, hipStream_t stream
   // merge runs over the decode kernel's records of split requests.
   DecodeArgs a = args;
   a.merge_splits = a.num_workers > 0 && a.new_k == nullptr && !a.partial_only && a.pre_parts == 0 &&
-                   a.num_seqs > a.num_workers;
+                   a.query_start_loc == nullptr && a.num_seqs > a.num_workers;
   if (bf16) {
     switch (decode_waves(a.num_kv_heads)) {
       case 1: launch_bf16_nw<D, 1>(a, stream); break;
@@ -1424,7 +1517,11 @@ hipError_t launch_decode_d(const DecodeArgs& args, bool bf16, hipStream_t stream
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 mgrid(a.num_q_heads, a.num_seqs);
-  if (a.num_workers > 0) {
+  if (a.query_start_loc != nullptr) {
+    hipLaunchKernelGGL((decode_merge_chunk_kernel<D>),
+                       dim3(a.num_seqs * a.n_cols, (a.num_q_heads + kMergeHeads - 1) / kMergeHeads),
+                       dim3(64 * kMergeHeads), 0, stream, a);
+  } else if (a.num_workers > 0) {
     dim3 hgrid((a.num_q_heads + kMergeHeads - 1) / kMergeHeads, a.merge_splits ? a.num_workers : a.num_seqs);
     // requests split over more than eight workers on average: the wide merge
     const bool wide = a.num_workers > 8 * a.num_seqs;

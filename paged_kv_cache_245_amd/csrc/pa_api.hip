@@ -182,6 +182,18 @@ DecodeLayout decode_layout(const pa_cache_desc* d, int32_t num_seqs, int32_t max
   return l;
 }
 
+// Short chunks through the balanced decode: its workspace with one partial row
+// per (request + worker, position, q head), positions up to max_query_len.
+DecodeLayout chunk_short_layout(const pa_cache_desc* d, int32_t num_seqs, int32_t max_query_len) {
+  DecodeLayout l{};
+  l.workers = balanced_workers(d);
+  const size_t rows = ((size_t)num_seqs + l.workers) * (size_t)max_query_len * d->num_q_heads;
+  l.acc_bytes = align256(rows * d->head_dim * sizeof(float));
+  l.ml_bytes = align256(rows * 2 * sizeof(float));
+  l.total = l.acc_bytes + l.ml_bytes + align256(((size_t)num_seqs + 1 + l.workers) * sizeof(int32_t));
+  return l;
+}
+
 // Shared-prefix decode: the balanced decode's workspace (for the tails), then the
 // prefix pass's partials [S][Hq][splits][D] and [S][Hq][splits][2]. The prefix
 // keys are split into ranges of whole 64-key tiles so that the prefix pass has
@@ -494,18 +506,23 @@ int pa_decode_append_lean(const pa_cache_desc* desc, void* out, const void* q, c
 }
 
 namespace {
-// pa_prefill_chunk; pa_prefill_chunk_append when new_k/new_v are given.
-int prefill_impl(const pa_cache_desc* desc, void* out, const void* q, const void* new_k, const void* new_v,
-                 const void* k_cache, const void* v_cache, const int32_t* query_start_loc,
-                 const int32_t* seq_lens, const int32_t* block_tables, int32_t max_blocks_per_seq,
-                 int32_t num_seqs, int32_t num_tokens, int32_t max_query_len, int32_t max_seq_len,
-                 float scale, void* stream) {
+// Arguments of the chunked prefill calls: PA_OK to launch, else the error. A call
+// with nothing to do returns PA_OK with *noop set.
+int check_prefill_args(const pa_cache_desc* desc, void* out, const void* q, const void* new_k,
+                       const void* k_cache, const void* v_cache, const int32_t* query_start_loc,
+                       const int32_t* seq_lens, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                       int32_t num_seqs, int32_t num_tokens, int32_t max_query_len, int32_t max_seq_len,
+                       float scale, void* stream, bool* noop) {
+  *noop = false;
   int st = validate_desc(desc);
   if (st != PA_OK) return st;
   if (desc->dtype != PA_BF16) return fail(PA_ERR_UNSUPPORTED, "prefill supports bf16 only");
   if (num_seqs < 0 || num_tokens < 0 || max_query_len < 0 || max_seq_len < 0)
     return fail(PA_ERR_INVALID_ARG, "negative size");
-  if (num_seqs == 0 || num_tokens == 0 || max_query_len == 0) return PA_OK;
+  if (num_seqs == 0 || num_tokens == 0 || max_query_len == 0) {
+    *noop = true;
+    return PA_OK;
+  }
   if (!out || !q || !k_cache || !v_cache || !query_start_loc || !seq_lens || !block_tables)
     return fail(PA_ERR_INVALID_ARG, "null pointer argument");
   if (max_blocks_per_seq <= 0) return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq must be positive");
@@ -548,6 +565,20 @@ int prefill_impl(const pa_cache_desc* desc, void* out, const void* q, const void
         }
     }
   }
+  return PA_OK;
+}
+
+// pa_prefill_chunk; pa_prefill_chunk_append when new_k/new_v are given.
+int prefill_impl(const pa_cache_desc* desc, void* out, const void* q, const void* new_k, const void* new_v,
+                 const void* k_cache, const void* v_cache, const int32_t* query_start_loc,
+                 const int32_t* seq_lens, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                 int32_t num_seqs, int32_t num_tokens, int32_t max_query_len, int32_t max_seq_len,
+                 float scale, void* stream) {
+  bool noop = false;
+  const int st = check_prefill_args(desc, out, q, new_k, k_cache, v_cache, query_start_loc, seq_lens, block_tables,
+                                    max_blocks_per_seq, num_seqs, num_tokens, max_query_len, max_seq_len, scale,
+                                    stream, &noop);
+  if (st != PA_OK || noop) return st;
   pa::PrefillArgs a{};
   a.q = (const uint16_t*)q;
   a.k = (const uint16_t*)k_cache;
@@ -592,6 +623,71 @@ int pa_prefill_chunk_append(const pa_cache_desc* desc, void* out, const void* q,
     return fail(PA_ERR_INVALID_ARG, "null pointer argument");
   return prefill_impl(desc, out, q, key, value, k_cache, v_cache, query_start_loc, seq_lens, block_tables,
                       max_blocks_per_seq, num_seqs, num_tokens, max_query_len, max_seq_len, scale, stream);
+}
+
+namespace {
+// Positions per request pa_prefill_chunk_short takes: the chunk's positions
+// times the group fill the 16 columns of the decode's score tile.
+int32_t chunk_short_max_rows(const pa_cache_desc* d) { return 16 / (d->num_q_heads / d->num_kv_heads); }
+}  // namespace
+
+int32_t pa_prefill_chunk_short_max_query_len(const pa_cache_desc* desc) {
+  const int st = validate_desc(desc);
+  if (st != PA_OK) return st;
+  if (desc->dtype != PA_BF16) return fail(PA_ERR_UNSUPPORTED, "prefill supports bf16 only");
+  return chunk_short_max_rows(desc);
+}
+
+size_t pa_prefill_chunk_short_workspace_size(const pa_cache_desc* desc, int32_t num_seqs,
+                                             int32_t max_query_len) {
+  if (validate_desc(desc) != PA_OK || desc->dtype != PA_BF16 || num_seqs <= 0 || max_query_len <= 0 ||
+      num_seqs > pa::decode_max_balanced_seqs() || max_query_len > chunk_short_max_rows(desc))
+    return 0;
+  return chunk_short_layout(desc, num_seqs, max_query_len).total;
+}
+
+int pa_prefill_chunk_short(const pa_cache_desc* desc, void* out, const void* q, const void* k_cache,
+                           const void* v_cache, const int32_t* query_start_loc, const int32_t* seq_lens,
+                           const int32_t* block_tables, int32_t max_blocks_per_seq, int32_t num_seqs,
+                           int32_t num_tokens, int32_t max_query_len, int32_t max_seq_len, float scale,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  bool noop = false;
+  int st = check_prefill_args(desc, out, q, nullptr, k_cache, v_cache, query_start_loc, seq_lens, block_tables,
+                              max_blocks_per_seq, num_seqs, num_tokens, max_query_len, max_seq_len, scale, stream,
+                              &noop);
+  if (st != PA_OK || noop) return st;
+  if (max_query_len > chunk_short_max_rows(desc))
+    return fail(PA_ERR_UNSUPPORTED, "max_query_len above " + std::to_string(chunk_short_max_rows(desc)) +
+                                        " (16 / q heads per kv head)");
+  if (num_seqs > pa::decode_max_balanced_seqs())
+    return fail(PA_ERR_UNSUPPORTED, "num_seqs above " + std::to_string(pa::decode_max_balanced_seqs()));
+  const DecodeLayout lay = chunk_short_layout(desc, num_seqs, max_query_len);
+  if (workspace == nullptr || workspace_bytes < lay.total)
+    return fail(PA_ERR_WORKSPACE, "workspace needs " + std::to_string(lay.total) + " bytes");
+  pa::DecodeArgs a{};
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.out = out;
+  a.block_tables = block_tables;
+  a.context_lens = seq_lens;
+  a.part_acc = (float*)workspace;
+  a.part_ml = (float*)((char*)workspace + lay.acc_bytes);
+  a.cum_blocks = (int32_t*)((char*)workspace + lay.acc_bytes + lay.ml_bytes);
+  a.split_req = a.cum_blocks + num_seqs + 1;
+  a.num_blocks = desc->num_blocks;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_seqs = num_seqs;
+  a.max_context_len = max_seq_len;
+  a.num_q_heads = desc->num_q_heads;
+  a.num_kv_heads = desc->num_kv_heads;
+  a.group = desc->num_q_heads / desc->num_kv_heads;
+  a.num_workers = lay.workers;
+  a.nontemporal = nontemporal_mode(desc, num_seqs, max_seq_len, true);
+  a.scale_log2 = scale * pa::kLog2e;
+  a.query_start_loc = query_start_loc;
+  a.n_cols = max_query_len;
+  return hip_status(pa::launch_decode(a, desc->head_dim, true, as_stream(stream)), "short-chunk launch");
 }
 
 int pa_copy_blocks(const pa_cache_desc* desc, void* k_cache, void* v_cache,

@@ -101,6 +101,13 @@ struct DecodeArgs {
   int32_t lean;              // balanced mode: the lean decode kernel (one wavefront per workgroup)
   int32_t ring_bytes;        // balanced mode: LDS bytes per wavefront for staged segment results
                              // (set at launch; 0 = each segment stores its result directly)
+  // Short-chunk mode (balanced bf16, pa_prefill_chunk_short; null and 0 otherwise): request s
+  // has query_start_loc[s+1] - query_start_loc[s] <= n_cols new tokens, its q rows from
+  // query_start_loc[s], all of them already in the pool (context_lens holds seq_lens).
+  // Column n of a kv head's score tile is (position n / group, q head n % group), and
+  // position p attends the keys before context_len - new tokens + p + 1.
+  const int32_t* query_start_loc;
+  int32_t n_cols;
   float scale_log2;  // scale * log2(e)
   // Append mode (balanced bf16 only; both null otherwise): [S][Hkv][D] K and V of
   // each request's newest token, position context_len - 1. The decode kernel

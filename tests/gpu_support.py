@@ -96,6 +96,21 @@ def run_prefill(w, d, k, v, device="cuda"):
     return out
 
 
+def run_prefill_short(w, d, k, v, device="cuda", max_query_len=None):
+    """pa_prefill_chunk_short over the workload's prefill chunks (max_query_len defaults to
+    the longest chunk)."""
+    p = w.prefill
+    q_t = device_tensor(p.q, w.spec.dtype, device)
+    out = torch.empty_like(q_t)
+    n = p.max_query_len if max_query_len is None else max_query_len
+    S = len(p.seq_lens)
+    ws = pa.chunk_short_workspace(d, S, n, device)
+    pa.pa_prefill_chunk_short(d, out, q_t, k, v, i32(p.query_start_loc, device), i32(p.seq_lens, device),
+                              i32(p.block_tables, device), n, p.max_seq_len, w.scale, ws)
+    torch.cuda.synchronize()
+    return out
+
+
 def run_prefill_append(w, d, k, v, device="cuda"):
     """pa_prefill_chunk_append with the chunks' new K/V (the first rows of the step's write,
     one per query row, in order); stores them into the pools."""

@@ -16,7 +16,7 @@ import torch
 import paged_kv_cache_245_amd as pa
 import workloads
 from gpu_support import (desc_of, device_tensor, gpu_pools, host_bits, i32, run_decode, run_prefill,
-                         run_prefill_append, say, write)
+                         run_prefill_append, run_prefill_short, say, write)
 
 pytestmark = pytest.mark.gpu
 
@@ -84,6 +84,18 @@ def test_prefill(D):
     d, kp, vp = gpu_pools(w)
     _, kz, vz = zero_pools(w)
     same_bits(run_prefill(w, d, kp, vp), run_prefill(w, d, kz, vz), "prefill")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_prefill_short(D):
+    """Short chunks through the decode kernel: contexts that end inside a block, and
+    positions whose causal limit falls inside a pair of blocks."""
+    say(f"  poison vs zeros: prefill_short D={D}")
+    w = workloads.custom_prefill(97 + D, cached=[0, 5, 63, 64, 100, 1000, 29], new=[1, 4, 3, 4, 2, 4, 4],
+                                 Hq=8, Hkv=2, D=D, dtype="bf16")
+    d, kp, vp = gpu_pools(w)
+    _, kz, vz = zero_pools(w)
+    same_bits(run_prefill_short(w, d, kp, vp), run_prefill_short(w, d, kz, vz), "prefill_short")
 
 
 @pytest.mark.parametrize("D", [64, 128])
