@@ -1065,39 +1065,94 @@ __global__ __launch_bounds__(64 * kMergeHeads) void decode_merge_balanced_kernel
     O[orow] = f32_to_bf16_bits(o[0] * inv);
 }
 
-// Short-chunk mode merge, one wavefront per (q head, request, position): the
+// Short-chunk mode merge, one wavefront per (q head, request, kP positions): the
 // partials of (request s, position p, head h) are rows ((s + w) n_cols + p) Hq + h
 // for the workers w0 .. w1 that read its blocks; a request read by one worker
-// was written by the decode kernel. Every position attends key 0, which the
-// first partial holds, so the fold's first batch has a finite maximum.
-template <int D>
+// was written by the decode kernel. The wavefront's lanes split into kP groups of
+// 64 / kP, one position each, every lane holding D kP / 64 dims, so that a
+// wavefront folds kP positions at once: the merge is a short chain of dependent
+// loads, and fewer, wider wavefronts wait through fewer rounds of it. Every
+// position attends key 0, which the first partial holds, so a fold's first batch
+// has a finite maximum.
+template <int D, int kP>
 __global__ __launch_bounds__(64 * kMergeHeads) void decode_merge_chunk_kernel(DecodeArgs a) {
-  constexpr int kE = D / 64;
+  constexpr int kLP = 64 / kP;  // lanes per position
+  constexpr int kE = D / kLP;   // dims per lane
+  constexpr int kBatch = 8;     // partials per round, all loads issued first
   const int lane = threadIdx.x & 63;
   const int h = blockIdx.y * kMergeHeads + (threadIdx.x >> 6);
-  if (h >= a.num_q_heads) return;  // whole wavefront; the kernel has no barrier
-  const int s = blockIdx.x / a.n_cols, p = blockIdx.x % a.n_cols;  // grid x: (request, position)
+  if (h >= a.num_q_heads) return;  // the kernel has no barrier and no cross-lane operation
+  const int groups = (a.n_cols + kP - 1) / kP;
+  const int s = blockIdx.x / groups;  // grid x: (request, group of kP positions)
+  const int pg = (blockIdx.x % groups) * kP;
+  const int p = pg + lane / kLP;
+  const int dim0 = (lane % kLP) * kE;
   const int q0 = a.query_start_loc[s], nq = a.query_start_loc[s + 1] - q0;
   const int L = min(a.context_lens[s], a.max_context_len);
   const int64_t T = a.cum_blocks[a.num_seqs];
   const int64_t c0 = a.cum_blocks[s], c1 = a.cum_blocks[s + 1];
-  if (p >= nq || L <= 0) return;  // no such position (a chunk with rows has keys)
+  if (p >= nq || p >= a.n_cols || L <= 0) return;  // no such position (a chunk with rows has keys)
   const int64_t Tn = max(T, (int64_t)1);
   const int W = (int)min((int64_t)a.num_workers, Tn);  // as in the decode kernel
   const int w0 = worker_of(c0, Tn, W);
   const int w1 = worker_of(max(c1 - 1, c0), Tn, W);
   if (w0 == w1) return;  // one segment: written by the decode kernel
+  const int np = w1 - w0 + 1;
   const int64_t rstep = (int64_t)a.n_cols * a.num_q_heads;
   const int64_t row0 = ((int64_t)s + w0) * rstep + (int64_t)p * a.num_q_heads + h;
-  float o[kE], den, M;
-  fold_partials<D>(a.part_acc, a.part_ml, row0, rstep, w1 - w0 + 1, lane, o, den, M);
+  float M = -INFINITY, den = 0.f, o[kE];
+#pragma unroll
+  for (int e = 0; e < kE; ++e) o[e] = 0.f;
+  for (int i0 = 0; i0 < np; i0 += kBatch) {
+    float mi[kBatch], li[kBatch], ai[kBatch][kE];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const bool in = i0 + j < np;
+      const int64_t r = row0 + (in ? i0 + j : 0) * rstep;
+      mi[j] = in ? a.part_ml[2 * r] : -INFINITY;
+      li[j] = in ? a.part_ml[2 * r + 1] : 0.f;
+      const float* src = a.part_acc + r * D + dim0;
+      if constexpr (kE % 4 == 0) {
+#pragma unroll
+        for (int v = 0; v < kE / 4; ++v) {
+          const f32x4 x = in ? *(const f32x4*)(src + 4 * v) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int t = 0; t < 4; ++t) ai[j][4 * v + t] = x[t];
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < kE; ++e) ai[j][e] = in ? src[e] : 0.f;
+      }
+    }
+    float mb = M;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) mb = fmaxf(mb, mi[j]);
+    const float alpha = fast_exp2(M - mb);  // 0 on the first round
+    den *= alpha;
+#pragma unroll
+    for (int e = 0; e < kE; ++e) o[e] *= alpha;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const float wgt = fast_exp2(mi[j] - mb);  // 0 for padding
+      den += wgt * li[j];
+#pragma unroll
+      for (int e = 0; e < kE; ++e) o[e] += wgt * ai[j][e];
+    }
+    M = mb;
+  }
   const float inv = 1.f / den;
-  uint16_t* O = (uint16_t*)a.out;
-  const int64_t orow = ((int64_t)(q0 + p) * a.num_q_heads + h) * D + kE * lane;
-  if constexpr (kE == 2)
-    *(uint32_t*)(O + orow) = pack_bf16x2(o[0] * inv, o[1] * inv);
-  else
-    O[orow] = f32_to_bf16_bits(o[0] * inv);
+  uint16_t* O = (uint16_t*)a.out + ((int64_t)(q0 + p) * a.num_q_heads + h) * D + dim0;
+  if constexpr (kE == 1) {
+    *O = f32_to_bf16_bits(o[0] * inv);
+  } else if constexpr (kE == 2) {
+    *(uint32_t*)O = pack_bf16x2(o[0] * inv, o[1] * inv);
+  } else if constexpr (kE == 4) {
+    *(u32x2*)O = u32x2{pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv)};
+  } else {
+    static_assert(kE == 8, "dims per lane");
+    *(u32x4*)O = u32x4{pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv),
+                       pack_bf16x2(o[4] * inv, o[5] * inv), pack_bf16x2(o[6] * inv, o[7] * inv)};
+  }
 }
 
 // Balanced mode merge for requests split over many workers (many partials each):
@@ -1518,9 +1573,15 @@ hipError_t launch_decode_d(const DecodeArgs& args, bool bf16, hipStream_t stream
   if (e != hipSuccess) return e;
   dim3 mgrid(a.num_q_heads, a.num_seqs);
   if (a.query_start_loc != nullptr) {
-    hipLaunchKernelGGL((decode_merge_chunk_kernel<D>),
-                       dim3(a.num_seqs * a.n_cols, (a.num_q_heads + kMergeHeads - 1) / kMergeHeads),
-                       dim3(64 * kMergeHeads), 0, stream, a);
+    // positions per wavefront: the chunk length's power of two, at most 4
+    const int kp = a.n_cols >= 3 ? 4 : a.n_cols;
+    const dim3 grid(a.num_seqs * ((a.n_cols + kp - 1) / kp), (a.num_q_heads + kMergeHeads - 1) / kMergeHeads);
+    if (kp == 4)
+      hipLaunchKernelGGL((decode_merge_chunk_kernel<D, 4>), grid, dim3(64 * kMergeHeads), 0, stream, a);
+    else if (kp == 2)
+      hipLaunchKernelGGL((decode_merge_chunk_kernel<D, 2>), grid, dim3(64 * kMergeHeads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_merge_chunk_kernel<D, 1>), grid, dim3(64 * kMergeHeads), 0, stream, a);
   } else if (a.num_workers > 0) {
     dim3 hgrid((a.num_q_heads + kMergeHeads - 1) / kMergeHeads, a.merge_splits ? a.num_workers : a.num_seqs);
     // requests split over more than eight workers on average: the wide merge

@@ -17,7 +17,11 @@ wavefronts fit beside the prefill's on every compute unit: the prefill keeps
 the matrix cores busy while the decode streams K/V from HBM. The two calls
 touch disjoint memory (the decode stores only into each one-token request's
 own last block; blocks shared with other requests are full and never
-written). Marshalling and sequencing only; the work runs in libpa.so's
+written). A step whose chunks are all short (at most 16 / (q heads per kv
+head) tokens, as when every request scores a few tokens at once) runs them
+through pa_prefill_chunk_short instead, on the caller's stream, followed by
+the decode: both calls then stream K/V from HBM, and running them side by side
+gains nothing. Marshalling and sequencing only; the work runs in libpa.so's
 kernels.
 """
 from __future__ import annotations
@@ -76,6 +80,13 @@ class StepRunner:
         self.meta = torch.empty(self.n_meta, dtype=torch.int32, device=self.device)
         self.ws = pa.decode_workspace(desc, max_seqs, max_blocks_per_seq * 16, 0, self.device)
         self.ws_bytes = 0 if self.ws is None else self.ws.numel()
+        # steps of short chunks: pa_prefill_chunk_short and its own workspace
+        self.short_rows = 0
+        self.ws_short = None
+        self.short_steps = 0  # steps whose chunks went through pa_prefill_chunk_short
+        if desc.dtype == pa.PA_BF16 and max_seqs <= 8192:
+            self.short_rows = pa.pa_prefill_chunk_short_max_query_len(desc)
+            self.ws_short = pa.chunk_short_workspace(desc, max_seqs, self.short_rows, self.device)
         # default priority, like every stream here
         self.side = side_stream if side_stream is not None else torch.cuda.Stream(self.device)
 
@@ -132,13 +143,21 @@ class StepRunner:
             need = pa.pa_decode_workspace_size(self.desc, S - P, int(batch.seq_lens[P:].max()))
             if need > self.ws_bytes:
                 raise ValueError("decode workspace too small for this step")
-        fork = P > 0 and S > P
+        longest = int(batch.counts[:P].max()) if P else 0
+        short = P > 0 and longest <= self.short_rows
+        fork = P > 0 and S > P and not short
         if P:
             pa.pa_write_kv(self.desc, key[:n_pf], value[:n_pf], self.k, self.v, slots[:n_pf])
             if fork:
                 self.side.wait_stream(stream)
-            pa.pa_prefill_chunk(self.desc, out[:n_pf], q[:n_pf], self.k, self.v, qsl, seq[:P], tables[:P],
-                                int(batch.counts[:P].max()), int(batch.seq_lens[:P].max()), self.scale)
+            if short:
+                self.short_steps += 1
+                pa.pa_prefill_chunk_short(self.desc, out[:n_pf], q[:n_pf], self.k, self.v, qsl, seq[:P],
+                                          tables[:P], longest, int(batch.seq_lens[:P].max()), self.scale,
+                                          self.ws_short)
+            else:
+                pa.pa_prefill_chunk(self.desc, out[:n_pf], q[:n_pf], self.k, self.v, qsl, seq[:P], tables[:P],
+                                    longest, int(batch.seq_lens[:P].max()), self.scale)
         if S > P:
             # a one-token request's new token is its newest, at position seq_len - 1
             args = (self.desc, out[n_pf:N], q[n_pf:N], key[n_pf:N], value[n_pf:N], self.k, self.v,

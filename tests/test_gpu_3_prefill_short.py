@@ -66,6 +66,16 @@ def test_one_request_all_workers():
     check(w, "one long request")
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_three_row_chunks(D):
+    """Chunks of at most 3 rows over split contexts: the merge's wavefronts take 4 positions,
+    the fourth of which no chunk has."""
+    say(f"  three-row chunks D={D}")
+    w = workloads.custom_prefill(519 + D, cached=[5000, 3000, 40, 7000], new=[3, 2, 3, 1], Hq=32, Hkv=8, D=D,
+                                 dtype="bf16")
+    check(w, f"three-row chunks D={D}")
+
+
 def test_positions_beyond_chunks():
     """max_query_len above every chunk: positions no chunk has are skipped, in the kernel
     and in the merge."""

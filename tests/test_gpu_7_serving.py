@@ -70,6 +70,20 @@ class Synth:
 def test_serving_trace_matches_oracle(num_blocks, budget, max_seqs, seed, num_host):
     say(f"serving trace: blocks {num_blocks}, budget {budget}, max_seqs {max_seqs}, seed {seed}, "
         f"swap space {num_host}")
+    run_trace(num_blocks, budget, max_seqs, seed, num_host)
+
+
+def test_serving_short_prompts():
+    """Prompts of 1-4 tokens, at most 6 requests at once: steps whose chunks are all short go
+    through pa_prefill_chunk_short, beside decodes once the first requests generate, and
+    must still match the oracle."""
+    say("serving trace: short prompts")
+    runner = run_trace(200, 64, 6, 6, 0, prompt_len=(1, 5), heads=(0,))
+    say(f"  {runner.short_steps} steps through the short-chunk call")
+    assert runner.short_steps > 0
+
+
+def run_trace(num_blocks, budget, max_seqs, seed, num_host, prompt_len=(1, 120), heads=(0, 16, 33, 40)):
     rng = np.random.default_rng(seed)
     synth = Synth(seed)
     pool = host.BlockPool(num_blocks, True, num_host)
@@ -78,8 +92,8 @@ def test_serving_trace_matches_oracle(num_blocks, budget, max_seqs, seed, num_ho
     shared = rng.integers(0, 500, 40).tolist()
     tokens, salts = {}, {}
     for i in range(12):
-        head = shared[:int(rng.choice([0, 16, 33, 40]))]
-        prompt = head + rng.integers(0, 500, int(rng.integers(1, 120))).tolist()
+        head = shared[:int(rng.choice(heads))]
+        prompt = head + rng.integers(0, 500, int(rng.integers(*prompt_len))).tolist()
         prompt = prompt[:num_blocks * 16 - 40]
         tokens[i], salts[i] = list(prompt), int(i % 2 == 0)
         sched.add_request(i, prompt, int(rng.integers(1, 24)), 0, salts[i])
@@ -149,3 +163,4 @@ def test_serving_trace_matches_oracle(num_blocks, budget, max_seqs, seed, num_ho
     if num_host:
         assert sched.num_swaps() > 0
     del mx, rel
+    return runner
