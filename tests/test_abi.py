@@ -155,6 +155,35 @@ def test_prefill_argument_checks(lib):
     assert call(desc(), T=0) == PA_OK
 
 
+def test_prefill_short_argument_checks(lib):
+    fake = ctypes.c_void_p(0x1000)
+
+    def call(d, ws=None, ws_bytes=0, **kw):
+        a = dict(max_blocks=512, S=64, T=256, mq=4, ms=4096, scale=0.088)
+        a.update(kw)
+        return lib.pa_prefill_chunk_short(ctypes.byref(d), fake, fake, fake, fake, fake, fake, fake,
+                                          a["max_blocks"], a["S"], a["T"], a["mq"], a["ms"], a["scale"],
+                                          ws, ws_bytes, None)
+
+    d = desc()  # 32 q / 8 kv heads: at most 4 rows per chunk
+    assert lib.pa_prefill_chunk_short_max_query_len(ctypes.byref(d)) == 4
+    assert lib.pa_prefill_chunk_short_max_query_len(ctypes.byref(desc(num_q_heads=8))) == 16
+    assert lib.pa_prefill_chunk_short_max_query_len(ctypes.byref(desc(dtype="f32"))) == UNSUPPORTED
+    need = lib.pa_prefill_chunk_short_workspace_size(ctypes.byref(d), 64, 4)
+    assert need > 0
+    assert lib.pa_prefill_chunk_short_workspace_size(ctypes.byref(d), 64, 5) == 0   # above 4 rows
+    assert lib.pa_prefill_chunk_short_workspace_size(ctypes.byref(d), 8193, 4) == 0
+    assert call(desc(dtype="f32")) == UNSUPPORTED
+    assert call(d, mq=5) == UNSUPPORTED
+    assert call(d, S=8193, T=8193) == UNSUPPORTED
+    assert call(d, ms=512 * 16 + 1) == INVALID
+    assert call(d, scale=float("inf")) == INVALID
+    assert call(d) == WORKSPACE
+    assert call(d, ws=fake, ws_bytes=need - 1) == WORKSPACE
+    assert call(d, S=0) == PA_OK
+    assert call(d, T=0) == PA_OK
+
+
 def test_write_kv_argument_checks(lib):
     fake = ctypes.c_void_p(0x1000)
     d = desc()

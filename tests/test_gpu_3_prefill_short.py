@@ -50,6 +50,27 @@ def test_many_requests_records():
     check(w, "600 short chunks")
 
 
+def test_most_requests():
+    """8,192 requests, the most the call takes: the block prefix sums fill 32 KiB of the
+    decode kernel's LDS beside its staged results; one more request is refused."""
+    rng = np.random.default_rng(520)
+    S = 8192
+    cached = rng.integers(0, 120, S)
+    new = rng.integers(1, 5, S)
+    say("  8,192 short chunks, G=4 D=64")
+    w = workloads.custom_prefill(520, cached=cached.tolist(), new=new.tolist(), Hq=8, Hkv=2, D=64, dtype="bf16")
+    d, k, v, out = check(w, "8,192 short chunks")
+    p = w.prefill
+    assert pa.pa_prefill_chunk_short_workspace_size(d, S + 1, 4) == 0
+    q = device_tensor(np.concatenate([p.q, p.q[:1]]), "bf16")
+    with pytest.raises(pa.PAError) as e:
+        pa.pa_prefill_chunk_short(d, torch.empty_like(q), q, k, v, i32(np.append(p.query_start_loc, q.shape[0])),
+                                  i32(np.append(p.seq_lens, 1)), i32(np.concatenate([p.block_tables,
+                                                                                     p.block_tables[:1]])),
+                                  4, p.max_seq_len, w.scale, pa.chunk_short_workspace(d, S, 4))
+    assert "num_seqs" in str(e.value)
+
+
 def test_long_contexts_split():
     """Long contexts split over many workers: the merge combines partials per (request,
     position, head); a chunk's first keys and its own rows land in different workers."""

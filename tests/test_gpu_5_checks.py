@@ -65,6 +65,33 @@ def test_check_mode_prefill(monkeypatch):
         assert e.value.status == RANGE
 
 
+def test_check_mode_prefill_short(monkeypatch):
+    """The short-chunk call checks the same metadata: rows past num_tokens, a sequence
+    shorter than its chunk, a chunk longer than max_query_len and an out-of-range block id
+    are refused before any launch; the good call then runs."""
+    w = workloads.custom_prefill(84, cached=[3, 40], new=[4, 2], Hq=8, Hkv=2, D=64, dtype="bf16")
+    d, k, v = gpu_pools(w)
+    monkeypatch.setenv("PA_CHECK", "1")
+    p = w.prefill
+    q = device_tensor(p.q, "bf16")
+    out = torch.empty_like(q)
+    ws = pa.chunk_short_workspace(d, 2, 4)
+    bt = p.block_tables.copy()
+    bt[1, 2] = w.spec.num_blocks + 1
+    for qsl, lens, tables, n in (([0, 4, 7], p.seq_lens, p.block_tables, 4),
+                                 ([0, 4, 6], [3, 42], p.block_tables, 4),
+                                 ([0, 4, 6], p.seq_lens, p.block_tables, 3),
+                                 ([0, 4, 6], p.seq_lens, bt, 4)):
+        with pytest.raises(pa.PAError) as e:
+            pa.pa_prefill_chunk_short(d, out, q, k, v, i32(qsl), i32(lens), i32(tables), n, p.max_seq_len,
+                                      w.scale, ws)
+        assert e.value.status == RANGE
+    pa.pa_prefill_chunk_short(d, out, q, k, v, i32(p.query_start_loc), i32(p.seq_lens), i32(p.block_tables), 4,
+                              p.max_seq_len, w.scale, ws)
+    torch.cuda.synchronize()
+    assert np.all(np.isfinite(as64(out)))
+
+
 def test_bad_block_id_without_check_gives_nan_not_fault():
     w = small()
     d, k, v = gpu_pools(w)
