@@ -133,18 +133,20 @@ class BlockPoolModel:
     def prefix_hit_tokens(self, rid) -> int:
         return BLOCK * len(self.prefix_hits(self.reqs[rid]))
 
-    def allocate_slots(self, rid, n_new):
-        """Returns the hit token count, or None when the free queue is too short."""
+    def allocate_slots(self, rid, n_new, lookahead=0):
+        """Returns the hit token count, or None when the free queue is too short.
+        lookahead: positions past the request's known tokens that the step also writes
+        (draft tokens of speculative decoding); the blocks cover them too."""
         r = self.reqs[rid]
         if r.swapped:
             raise ValueError("request is swapped out")
         hits = self.prefix_hits(r)
         start = r.computed + BLOCK * len(hits)
         total = start + n_new
-        if n_new < 0 or total > len(r.tokens):
+        if n_new < 0 or lookahead < 0 or total > len(r.tokens):
             raise ValueError("allocation beyond the request's tokens")
-        fresh = max(0, ceil_blocks(total) - len(r.blocks) - len(hits))
-        copy = self.needs_copy(r, start, n_new)
+        fresh = max(0, ceil_blocks(total + lookahead) - len(r.blocks) - len(hits))
+        copy = self.needs_copy(r, start, n_new + lookahead)
         need = fresh + int(copy) + sum(1 for b in hits if self.ref[b] == 0)
         if need > len(self.free):
             return None

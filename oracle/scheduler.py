@@ -18,6 +18,9 @@ when the blocks run out"):
   * The preempted request may instead keep its K/V by swapping it to CPU memory
     (aitrending, "The 1960s Operating System Trick That Makes vLLM 4x Faster",
     Technical Details: swap or recompute).
+  * A request is a pair (tokens computed, tokens known plus speculative tokens):
+    a running request may carry draft tokens for the next step, which the step
+    computes after its known tokens, budget permitting.
 
 Readings where the pages are silent (the same as the library's): no admission
 in a step that preempted; without chunked prefill, admission stops at the first
@@ -28,7 +31,17 @@ max_new_tokens-th generated token, which is not appended; the batch lists the
 requests given more than one token first, then the one-token ones; in swap mode
 the victim is swapped out when the swap space has room (else recomputed), and a
 swapped request is admitted only when the free queue covers its swap-in and the
-blocks of the tokens it is given, resuming at its computed count.
+blocks of the tokens it is given, resuming at its computed count. Drafts: they
+are set for one step and dropped at its update; only a running request whose
+known tokens all fit the step gets them (as many as the budget leaves), and its
+blocks then cover them too; the update takes, per request, how many of the
+scheduled drafts were accepted (a prefix of them) and the token sampled after
+the last accepted one; the accepted drafts join the request's tokens as
+computed (their K/V was written by the step), then the sampled token is
+appended; each of these counts as one generated token, and the request
+finishes at its max_new_tokens-th as before (that token is not appended, and
+the rest of the step's tokens for it are dropped). Rejected drafts leave K/V in
+slots past the computed count, which later steps overwrite.
 """
 from __future__ import annotations
 
@@ -50,6 +63,8 @@ class SchedulerModel:
         self.waiting = []    # head first
         self.running = []    # start order
         self.plan = []       # (id, start, count), batch order
+        self.drafts = {}     # id -> draft tokens for the next step
+        self.plan_drafts = []  # drafts scheduled per plan item (the last ones of its count)
         self.finished = []
         self.preemptions = 0
         self.swaps = 0
@@ -84,8 +99,14 @@ class SchedulerModel:
         self.arrivals += 1
         self.enqueue(rid, False)
 
+    def set_spec_tokens(self, rid, drafts):
+        if rid not in self.info:
+            raise ValueError("unknown request")
+        self.drafts[rid] = list(drafts)
+
     def schedule(self):
         order = []
+        look = {}  # id -> drafts scheduled
         budget = self.budget
         preempted = False
         i = 0
@@ -93,12 +114,14 @@ class SchedulerModel:
             rid = self.running[i]
             r = self.pool.reqs[rid]
             start = r.computed
-            n = min(len(r.tokens) - start, budget)
+            real = len(r.tokens) - start
+            k = len(self.drafts.get(rid, ())) if real >= 1 else 0
+            n = min(real + k, budget)
             if n <= 0:
                 i += 1
                 continue
             gone = False
-            while self.pool.allocate_slots(rid, n) is None:
+            while self.pool.allocate_slots(rid, min(n, real), n - min(n, real)) is None:
                 v = self.victim()
                 vi = self.running.index(v)
                 self.running.remove(v)
@@ -122,6 +145,7 @@ class SchedulerModel:
             if gone:
                 continue
             order.append((rid, start, n))
+            look[rid] = n - min(n, real)
             budget -= n
             i += 1
         while (not preempted and self.waiting and budget > 0
@@ -155,6 +179,7 @@ class SchedulerModel:
             order.append((rid, hit, n))
             budget -= n
         self.plan = [x for x in order if x[2] > 1] + [x for x in order if x[2] == 1]
+        self.plan_drafts = [look.get(x[0], 0) for x in self.plan]
         return list(self.plan)
 
     def batch(self, pad_block=0):
@@ -172,22 +197,34 @@ class SchedulerModel:
             pos += list(range(start, start + n))
         return qsl, seq, tables, slots, pos
 
-    def update(self, sampled):
+    def update(self, sampled, accepted=None):
+        """accepted[i]: how many of plan item i's scheduled drafts were accepted (None: none)."""
         done = 0
         for i, (rid, start, n) in enumerate(self.plan):
+            d = self.plan_drafts[i]
+            a = 0 if accepted is None else accepted[i]
+            if not 0 <= a <= d:
+                raise ValueError("accepted drafts out of range")
             r = self.pool.reqs[rid]
-            self.pool.commit(rid, start + n)
-            if start + n < len(r.tokens):
+            c = start + n - d  # the known tokens computed
+            self.pool.commit(rid, c)
+            if c < len(r.tokens):
                 continue
             info = self.info[rid]
-            info["produced"] += 1
-            if info["produced"] >= info["max_new"]:
-                self.pool.free_request(rid)
-                self.running.remove(rid)
-                del self.info[rid]
-                self.finished.append(rid)
-                done += 1
-            else:
-                self.pool.append_tokens(rid, [sampled[i]])
+            outs = self.drafts[rid][:a] + [sampled[i]] if a else [sampled[i]]
+            for j, t in enumerate(outs):
+                info["produced"] += 1
+                if info["produced"] >= info["max_new"]:
+                    self.pool.free_request(rid)
+                    self.running.remove(rid)
+                    del self.info[rid]
+                    self.finished.append(rid)
+                    done += 1
+                    break
+                self.pool.append_tokens(rid, [t])
+                if j < a:  # an accepted draft: its K/V is in the pool already
+                    self.pool.commit(rid, c + j + 1)
         self.plan = []
+        self.plan_drafts = []
+        self.drafts = {}
         return done

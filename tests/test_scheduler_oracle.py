@@ -208,13 +208,105 @@ def pin_trace_completes_and_reads_back():
         assert produced == max_new
 
 
+# ---- speculative tokens: a request is (tokens computed, tokens known plus drafts)
+
+def spec_step(s, dev, rng, produced, max_new):
+    """One step with random drafts (0-3 tokens, ids 100-109, never a sampled id) for every
+    running request and a random number of them accepted; the simulated device gets every
+    scheduled position's token id, drafts included."""
+    for rid in list(s.running):
+        s.set_spec_tokens(rid, [rng.randint(100, 109) for _ in range(rng.randint(0, 3))])
+    plan = s.schedule()
+    apply_ops(s.pool.take_ops(), dev, {})
+    _, _, _, slots, pos = s.batch()
+    k = 0
+    accepted = []
+    for (rid, start, n), d in zip(plan, s.plan_drafts):
+        toks = s.pool.reqs[rid].tokens + s.drafts.get(rid, [])[:d]
+        for j in range(n):
+            dev[slots[k]] = toks[pos[k]]
+            k += 1
+        a = rng.randint(0, d)
+        accepted.append(a)
+        if start + n - d == len(s.pool.reqs[rid].tokens):
+            produced[rid] = min(produced.get(rid, 0) + a + 1, max_new[rid])
+    assert sum(n for _, _, n in plan) <= s.budget
+    s.update([rng.randint(0, 99) for _ in plan], accepted)
+    return plan
+
+
+def pin_drafts_follow_the_known_tokens():
+    s = make(64, 64)
+    s.add_request(1, list(range(20)), 9)
+    step(s)                                       # the prompt; 7 is sampled
+    s.set_spec_tokens(1, [101, 102, 103])
+    assert s.schedule() == [(1, 20, 4)] and s.plan_drafts == [3]
+    _, seq, _, slots, pos = s.batch()
+    assert seq == [24] and pos == [20, 21, 22, 23]
+    s.update([9], [2])                            # two drafts accepted, then 9 sampled
+    r = s.pool.reqs[1]
+    assert r.tokens == list(range(20)) + [7, 101, 102, 9] and r.computed == 23
+    assert s.schedule() == [(1, 23, 1)] and s.plan_drafts == [0]  # drafts last one step
+
+
+def pin_drafts_fit_the_budget():
+    s = make(64, 3)
+    s.add_request(1, [5], 9)
+    step(s)
+    s.set_spec_tokens(1, [101, 102, 103, 104])
+    assert s.schedule() == [(1, 1, 3)] and s.plan_drafts == [2]
+    s.update([9], [0])                            # none accepted: only the sampled token
+    assert s.pool.reqs[1].tokens == [5, 7, 9] and s.pool.reqs[1].computed == 2
+
+
+def pin_a_prompt_catching_up_gets_no_drafts():
+    s = make(64, 32)
+    s.add_request(1, list(range(100)), 3)
+    s.set_spec_tokens(1, [101])
+    assert s.schedule() == [(1, 0, 32)] and s.plan_drafts == [0]
+
+
+def pin_accepted_drafts_count_as_generated():
+    s = make(64, 64)
+    s.add_request(1, list(range(20)), 3)
+    step(s)                                       # first generated token
+    s.set_spec_tokens(1, [101, 102, 103])
+    s.schedule()
+    assert s.update([9], [3]) == 1                # 101, 102 make 3: finished, 102 not appended
+    assert s.finished == [1] and 1 not in s.pool.reqs
+
+
+def pin_spec_trace_reads_back():
+    """Random drafts and acceptance: every computed position holds its token (a rejected
+    draft is never counted as computed), and every request makes exactly its tokens."""
+    for seed in range(16):
+        rng = random.Random(100 + seed)
+        s = make(rng.choice([10, 16, 40]), rng.choice([8, 24, 48]), max_seqs=rng.choice([2, 8]),
+                 policy=rng.choice([sm.FCFS, sm.PRIORITY]))
+        dev, produced, max_new = {}, {}, {}
+        for i in range(10):
+            max_new[i] = rng.randint(1, 12)
+            s.add_request(i, [rng.randint(0, 99) for _ in range(rng.randint(1, 40))], max_new[i],
+                          priority=rng.randint(0, 2))
+        for _ in range(2000):
+            spec_step(s, dev, rng, produced, max_new)
+            assert readback_ok(s, dev)
+            if not s.running and not s.waiting:
+                break
+        assert sorted(s.finished) == list(range(10))
+        assert produced == max_new
+
+
 ALL_PINS = [pin_chunked_prefill_splits_a_long_prompt, pin_steps_mix_prompts_and_generation,
             pin_running_served_before_waiting, pin_budget_is_never_exceeded,
             pin_preemption_takes_the_newest_and_requeues_it_first,
             pin_priority_preempts_lowest_priority_latest_arrival,
             pin_finished_requests_release_their_blocks, pin_no_admission_beyond_max_seqs,
             pin_swap_mode_resumes_where_it_stopped, pin_swap_mode_without_room_recomputes,
-            pin_without_chunking_a_prompt_waits_for_room, pin_trace_completes_and_reads_back]
+            pin_without_chunking_a_prompt_waits_for_room, pin_trace_completes_and_reads_back,
+            pin_drafts_follow_the_known_tokens, pin_drafts_fit_the_budget,
+            pin_a_prompt_catching_up_gets_no_drafts, pin_accepted_drafts_count_as_generated,
+            pin_spec_trace_reads_back]
 
 
 @pytest.mark.parametrize("pin", ALL_PINS, ids=lambda f: f.__name__)
@@ -244,13 +336,35 @@ def _no_chunking(self):
         self.budget = saved
 
 
-def _keep_finished_blocks(self, sampled):
+def _keep_finished_blocks(self, sampled, accepted=None):
     free = self.pool.free_request
     self.pool.free_request = lambda rid, keep=False: None if not keep else free(rid, keep)
     try:
-        return _orig_update(self, sampled)
+        return _orig_update(self, sampled, accepted)
     finally:
         self.pool.free_request = free
+
+
+def _rejected_drafts_committed(self, sampled, accepted=None):
+    # every scheduled position counted as computed once the tokens reach it: the
+    # sampled token's position then claims the first rejected draft's K/V
+    plan = list(self.plan)
+    done = _orig_update(self, sampled, accepted)
+    for rid, start, n in plan:
+        r = self.pool.reqs.get(rid)
+        if r is not None:
+            self.pool.commit(rid, max(r.computed, min(start + n, len(r.tokens), 16 * len(r.blocks))))
+    return done
+
+
+def _drafts_ignore_the_budget(self):
+    saved = self.budget
+    extra = sum(len(d) for d in self.drafts.values())
+    self.budget = saved + extra  # the drafts come on top of the budget
+    try:
+        return _orig_schedule(self)
+    finally:
+        self.budget = saved
 
 
 def _swap_ignored(self):
@@ -265,6 +379,8 @@ MISTAKES.update({
     "whole prompts ignore the budget": ("schedule", _no_chunking),
     "finished requests keep their blocks": ("update", _keep_finished_blocks),
     "swap mode recomputes instead": ("schedule", _swap_ignored),
+    "rejected drafts counted as computed": ("update", _rejected_drafts_committed),
+    "drafts on top of the budget": ("schedule", _drafts_ignore_the_budget),
 })
 
 
