@@ -93,6 +93,15 @@ int64_t pa_pool_prefix_hit_tokens(const pa_block_pool* pool, int64_t req_id);
  * an error (computed + hits + num_new_tokens beyond the request's tokens). */
 int pa_pool_allocate_slots(pa_block_pool* pool, int64_t req_id, int64_t num_new_tokens,
                            int64_t* hit_tokens);
+/* pa_pool_allocate_slots whose blocks also cover num_lookahead positions past the
+ * new tokens, which may lie past the request's known tokens: speculative draft
+ * tokens that the step writes K/V for and that become tokens only when accepted
+ * (the teardown's requests are (computed, known plus speculative) pairs:
+ * "Continuous batching: rebuild the batch every step"). Their slots are
+ * readable through pa_pool_slot_mapping; pa_pool_commit never counts them until
+ * they are appended as tokens. */
+int pa_pool_allocate_slots_lookahead(pa_block_pool* pool, int64_t req_id, int64_t num_new_tokens,
+                                     int64_t num_lookahead, int64_t* hit_tokens);
 
 /* Record that the first num_computed tokens now hold K/V in the pool (never
  * decreasing, at most the tokens the blocks cover). Every block that became

@@ -34,6 +34,17 @@
  *   - When a request's computed count reaches its token count, the step's
  *     sampled token for it is appended; it finishes when it has produced
  *     max_new_tokens tokens (the last one is not appended).
+ *   - Speculative tokens (the teardown's request is a pair of computed tokens
+ *     and known tokens plus speculative ones, "Continuous batching: rebuild
+ *     the batch every step"): draft tokens set for a request hold for the next
+ *     step only. A running request whose known tokens all fit the step gets as
+ *     many of its drafts as the budget leaves, after its known tokens, and its
+ *     blocks cover them; a request still catching up, or not yet running, gets
+ *     none. The update takes how many of each request's scheduled drafts were
+ *     accepted (a prefix of them): those join the request's tokens as computed,
+ *     then the token sampled after them is appended; each counts as a
+ *     generated token, up to max_new_tokens. Rejected drafts leave K/V past the
+ *     computed count, which later steps overwrite.
  *
  * The step's batch is laid out for one pa_write_kv and one pa_prefill_chunk (the
  * requests given more than one token) and one pa_decode_append (those given
@@ -84,12 +95,18 @@ int pa_sched_add_request(pa_scheduler* sched, int64_t req_id, const int32_t* pro
                          int64_t num_tokens, int32_t max_new_tokens, int32_t priority,
                          int64_t cache_salt);
 
+/* Draft tokens [num_drafts >= 0] of a queued request for the next step
+ * (replacing any set before); dropped at the next pa_sched_update. */
+int pa_sched_set_spec_tokens(pa_scheduler* sched, int64_t req_id, const int32_t* drafts, int32_t num_drafts);
+
 /* Plan the next step; returns the number of scheduled requests or an error.
  * The plan stays readable until the next pa_sched_schedule. */
 int64_t pa_sched_schedule(pa_scheduler* sched);
 
 /* The plan, in batch order: request id, first new position, new token count. */
 int pa_sched_plan(const pa_scheduler* sched, int64_t* req_ids, int32_t* starts, int32_t* counts);
+/* Draft tokens scheduled per plan entry: the last drafts[i] of counts[i]. */
+int pa_sched_plan_drafts(const pa_scheduler* sched, int32_t* drafts);
 int64_t pa_sched_plan_tokens(const pa_scheduler* sched);   /* new tokens in the step */
 int64_t pa_sched_plan_prefills(const pa_scheduler* sched); /* leading requests with > 1 token */
 int32_t pa_sched_plan_max_blocks(const pa_scheduler* sched); /* widest block table in the step */
@@ -111,6 +128,11 @@ int pa_sched_batch(const pa_scheduler* sched, int32_t* query_start_loc, int32_t*
  * computed count reached their token count), and finish requests that reached
  * max_new_tokens (their blocks are released). Returns the number finished. */
 int64_t pa_sched_update(pa_scheduler* sched, const int32_t* sampled);
+/* pa_sched_update after a step with draft tokens: num_accepted[i] (plan order,
+ * 0 .. drafts[i]) of entry i's scheduled drafts were accepted, and sampled[i]
+ * is the token sampled after the last accepted one. NULL num_accepted: none.
+ * An out-of-range count is refused before anything changes. */
+int64_t pa_sched_update_spec(pa_scheduler* sched, const int32_t* sampled, const int32_t* num_accepted);
 
 int64_t pa_sched_num_waiting(const pa_scheduler* sched);
 int64_t pa_sched_num_running(const pa_scheduler* sched);

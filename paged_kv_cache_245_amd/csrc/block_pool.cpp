@@ -254,8 +254,13 @@ int64_t pa_pool_prefix_hit_tokens(const pa_block_pool* pool, int64_t req_id) {
 
 int pa_pool_allocate_slots(pa_block_pool* pool, int64_t req_id, int64_t num_new_tokens,
                            int64_t* hit_tokens) {
+  return pa_pool_allocate_slots_lookahead(pool, req_id, num_new_tokens, 0, hit_tokens);
+}
+
+int pa_pool_allocate_slots_lookahead(pa_block_pool* pool, int64_t req_id, int64_t num_new_tokens,
+                                     int64_t num_lookahead, int64_t* hit_tokens) {
   if (pool == nullptr) return fail(PA_POOL_ERR_INVALID_ARG, "null pointer");
-  if (num_new_tokens < 0) return fail(PA_POOL_ERR_INVALID_ARG, "negative token count");
+  if (num_new_tokens < 0 || num_lookahead < 0) return fail(PA_POOL_ERR_INVALID_ARG, "negative token count");
   Request* rp = pool->find(req_id);
   if (rp == nullptr) return unknown(req_id);
   Request& r = *rp;
@@ -266,10 +271,10 @@ int pa_pool_allocate_slots(pa_block_pool* pool, int64_t req_id, int64_t num_new_
   if (total > (int64_t)r.tokens.size())
     return fail(PA_POOL_ERR_RANGE, "allocation beyond the request's tokens");
   const int64_t held = (int64_t)r.blocks.size() + (int64_t)hits.size();
-  const int64_t fresh = std::max<int64_t>(0, (total + kB - 1) / kB - held);
+  const int64_t fresh = std::max<int64_t>(0, (total + num_lookahead + kB - 1) / kB - held);
   // copy-on-write: new tokens start inside a partly filled block that others share
   const int64_t first = start / kB;
-  const bool cow = num_new_tokens > 0 && start % kB != 0 && first < (int64_t)r.blocks.size() &&
+  const bool cow = num_new_tokens + num_lookahead > 0 && start % kB != 0 && first < (int64_t)r.blocks.size() &&
                    pool->blocks[r.blocks[first]].ref > 1;
   int64_t from_queue = fresh + (cow ? 1 : 0);
   for (int32_t id : hits)

@@ -7,7 +7,9 @@
 // running request (FCFS) or of the lowest-priority, latest-arrival one
 // (priority), which returns to the waiting queue with nothing computed, or,
 // in swap mode, with its computed K/V swapped out to host memory; then, unless
-// the step preempted, waiting requests are admitted in queue order.
+// the step preempted, waiting requests are admitted in queue order. A running
+// request may also carry draft tokens for one step (speculative decoding): the
+// teardown's request is a (computed, known plus speculative) pair.
 #include "pa_sched.h"
 
 #include <algorithm>
@@ -36,6 +38,7 @@ struct SchedRequest {
 struct Item {
   int64_t id;
   int32_t start, count;
+  int32_t drafts;  // the last `drafts` positions of count are draft tokens
 };
 
 }  // namespace
@@ -47,6 +50,7 @@ struct pa_scheduler {
   std::deque<int64_t> waiting;   // head first
   std::vector<int64_t> running;  // start order
   std::vector<Item> plan;        // batch order
+  std::unordered_map<int64_t, std::vector<int32_t>> drafts;  // for the next step
   std::deque<int64_t> finished;
   int64_t preemptions = 0;
   int64_t swaps = 0;
@@ -113,6 +117,14 @@ int pa_sched_add_request(pa_scheduler* s, int64_t req_id, const int32_t* prompt,
   return PA_POOL_OK;
 }
 
+int pa_sched_set_spec_tokens(pa_scheduler* s, int64_t req_id, const int32_t* drafts, int32_t num_drafts) {
+  if (s == nullptr || num_drafts < 0 || (num_drafts > 0 && drafts == nullptr))
+    return fail(PA_POOL_ERR_INVALID_ARG, "bad draft tokens");
+  if (s->reqs.count(req_id) == 0) return fail(PA_POOL_ERR_INVALID_ARG, "unknown request");
+  s->drafts[req_id].assign(drafts, drafts + num_drafts);
+  return PA_POOL_OK;
+}
+
 int64_t pa_sched_schedule(pa_scheduler* s) {
   if (s == nullptr) return fail(PA_POOL_ERR_INVALID_ARG, "null scheduler");
   std::vector<Item> order;  // scheduling order
@@ -125,14 +137,18 @@ int64_t pa_sched_schedule(pa_scheduler* s) {
     const int64_t id = s->running[i];
     const int64_t computed = pa_pool_request_computed(s->pool, id);
     const int64_t lacking = pa_pool_request_tokens(s->pool, id) - computed;
-    const int64_t n = std::min(lacking, budget);
+    // draft tokens follow the known ones, as far as the budget goes
+    auto dr = s->drafts.find(id);
+    const int64_t k = (lacking >= 1 && dr != s->drafts.end()) ? (int64_t)dr->second.size() : 0;
+    const int64_t n = std::min(lacking + k, budget);
+    const int64_t known = std::min(n, lacking);
     if (n <= 0) {
       ++i;
       continue;
     }
     bool self_preempted = false;
     for (;;) {
-      const int st = pa_pool_allocate_slots(s->pool, id, n, nullptr);
+      const int st = pa_pool_allocate_slots_lookahead(s->pool, id, known, n - known, nullptr);
       if (st == PA_POOL_OK) break;
       if (st != PA_POOL_NO_SPACE) return fail(st, pa_pool_last_error());
       const size_t v = s->victim_index();
@@ -161,7 +177,7 @@ int64_t pa_sched_schedule(pa_scheduler* s) {
       if (v < i) --i;
     }
     if (self_preempted) continue;  // running[i] is now the next request
-    order.push_back(Item{id, (int32_t)computed, (int32_t)n});
+    order.push_back(Item{id, (int32_t)computed, (int32_t)n, (int32_t)(n - known)});
     budget -= n;
     ++i;
   }
@@ -184,7 +200,7 @@ int64_t pa_sched_schedule(pa_scheduler* s) {
       if (st != PA_POOL_OK) return fail(st < 0 ? st : PA_POOL_ERR_INVALID_ARG, "swap-in admission failed");
       s->waiting.pop_front();
       s->running.push_back(id);
-      order.push_back(Item{id, (int32_t)computed, (int32_t)n});
+      order.push_back(Item{id, (int32_t)computed, (int32_t)n, 0});
       budget -= n;
       continue;
     }
@@ -197,7 +213,7 @@ int64_t pa_sched_schedule(pa_scheduler* s) {
     if (st != PA_POOL_OK) return fail(st, pa_pool_last_error());
     s->waiting.pop_front();
     s->running.push_back(id);
-    order.push_back(Item{id, (int32_t)hit, (int32_t)n});
+    order.push_back(Item{id, (int32_t)hit, (int32_t)n, 0});
     budget -= n;
   }
 
@@ -216,6 +232,12 @@ int pa_sched_plan(const pa_scheduler* s, int64_t* req_ids, int32_t* starts, int3
     if (starts) starts[i] = s->plan[i].start;
     if (counts) counts[i] = s->plan[i].count;
   }
+  return PA_POOL_OK;
+}
+
+int pa_sched_plan_drafts(const pa_scheduler* s, int32_t* drafts) {
+  if (s == nullptr || drafts == nullptr) return fail(PA_POOL_ERR_INVALID_ARG, "null pointer");
+  for (size_t i = 0; i < s->plan.size(); ++i) drafts[i] = s->plan[i].drafts;
   return PA_POOL_OK;
 }
 
@@ -270,28 +292,45 @@ int pa_sched_batch(const pa_scheduler* s, int32_t* query_start_loc, int32_t* seq
 }
 
 int64_t pa_sched_update(pa_scheduler* s, const int32_t* sampled) {
+  return pa_sched_update_spec(s, sampled, nullptr);
+}
+
+int64_t pa_sched_update_spec(pa_scheduler* s, const int32_t* sampled, const int32_t* num_accepted) {
   if (s == nullptr) return fail(PA_POOL_ERR_INVALID_ARG, "null scheduler");
+  for (size_t i = 0; num_accepted != nullptr && i < s->plan.size(); ++i)
+    if (num_accepted[i] < 0 || num_accepted[i] > s->plan[i].drafts)
+      return fail(PA_POOL_ERR_INVALID_ARG, "num_accepted[" + std::to_string(i) + "] is outside [0, drafts]");
   int64_t done = 0;
   for (size_t i = 0; i < s->plan.size(); ++i) {
     const Item& x = s->plan[i];
-    const int64_t c = (int64_t)x.start + x.count;
+    const int64_t c = (int64_t)x.start + x.count - x.drafts;  // the known tokens computed
     int st = pa_pool_commit(s->pool, x.id, c);
     if (st != PA_POOL_OK) return fail(st, pa_pool_last_error());
     if (c < pa_pool_request_tokens(s->pool, x.id)) continue;  // still catching up
+    // generated this step: the accepted drafts, then the token sampled after them
+    const int32_t a = num_accepted != nullptr ? num_accepted[i] : 0;
     SchedRequest& r = s->reqs.at(x.id);
-    if (++r.produced >= r.max_new) {
-      pa_pool_free_request(s->pool, x.id, 0);
-      s->running.erase(std::find(s->running.begin(), s->running.end(), x.id));
-      s->reqs.erase(x.id);
-      s->finished.push_back(x.id);
-      ++done;
-    } else {
-      if (sampled == nullptr) return fail(PA_POOL_ERR_INVALID_ARG, "sampled tokens needed");
-      st = pa_pool_append_tokens(s->pool, x.id, &sampled[i], 1);
+    for (int32_t j = 0; j <= a; ++j) {
+      if (++r.produced >= r.max_new) {
+        pa_pool_free_request(s->pool, x.id, 0);
+        s->running.erase(std::find(s->running.begin(), s->running.end(), x.id));
+        s->reqs.erase(x.id);
+        s->finished.push_back(x.id);
+        ++done;
+        break;
+      }
+      if (j < a) {  // an accepted draft: its K/V is in the pool already
+        st = pa_pool_append_tokens(s->pool, x.id, &s->drafts.at(x.id)[j], 1);
+        if (st == PA_POOL_OK) st = pa_pool_commit(s->pool, x.id, c + j + 1);
+      } else {
+        if (sampled == nullptr) return fail(PA_POOL_ERR_INVALID_ARG, "sampled tokens needed");
+        st = pa_pool_append_tokens(s->pool, x.id, &sampled[i], 1);
+      }
       if (st != PA_POOL_OK) return fail(st, pa_pool_last_error());
     }
   }
   s->plan.clear();
+  s->drafts.clear();
   return done;
 }
 

@@ -21,7 +21,8 @@ BLOCK_SIZE = 16
 OP_COPY, OP_SWAP_OUT, OP_SWAP_IN = 0, 1, 2  # kinds of block operations (pa_pool_take_ops)
 
 POOL_EXPORTED = ("pa_pool_create", "pa_pool_destroy", "pa_pool_add_request", "pa_pool_append_tokens",
-                 "pa_pool_prefix_hit_tokens", "pa_pool_allocate_slots", "pa_pool_commit",
+                 "pa_pool_prefix_hit_tokens", "pa_pool_allocate_slots", "pa_pool_allocate_slots_lookahead",
+                 "pa_pool_commit",
                  "pa_pool_free_request", "pa_pool_fork", "pa_pool_take_ops", "pa_pool_num_blocks",
                  "pa_pool_num_free_blocks", "pa_pool_num_cached_blocks", "pa_pool_ref_count",
                  "pa_pool_request_tokens", "pa_pool_request_computed", "pa_pool_block_table",
@@ -55,6 +56,7 @@ def load_host():
         "pa_pool_append_tokens": (ctypes.c_int, [P, I64, PI32, I64]),
         "pa_pool_prefix_hit_tokens": (I64, [P, I64]),
         "pa_pool_allocate_slots": (ctypes.c_int, [P, I64, I64, PI64]),
+        "pa_pool_allocate_slots_lookahead": (ctypes.c_int, [P, I64, I64, I64, PI64]),
         "pa_pool_commit": (ctypes.c_int, [P, I64, I64]),
         "pa_pool_free_request": (ctypes.c_int, [P, I64, I32]),
         "pa_pool_fork": (ctypes.c_int, [P, I64, I64]),
@@ -135,11 +137,13 @@ class BlockPool:
     def prefix_hit_tokens(self, req_id: int) -> int:
         return _check(self._lib.pa_pool_prefix_hit_tokens(self._p, req_id), "pa_pool_prefix_hit_tokens")
 
-    def allocate_slots(self, req_id: int, num_new_tokens: int):
-        """Hit token count, or None when the free queue is too short (nothing changed)."""
+    def allocate_slots(self, req_id: int, num_new_tokens: int, lookahead: int = 0):
+        """Hit token count, or None when the free queue is too short (nothing changed).
+        lookahead: positions past the new tokens (draft tokens) the blocks also cover."""
         hit = ctypes.c_int64(0)
-        st = _check(self._lib.pa_pool_allocate_slots(self._p, req_id, num_new_tokens, ctypes.byref(hit)),
-                    "pa_pool_allocate_slots")
+        st = _check(self._lib.pa_pool_allocate_slots_lookahead(self._p, req_id, num_new_tokens, lookahead,
+                                                               ctypes.byref(hit)),
+                    "pa_pool_allocate_slots_lookahead")
         return None if st == POOL_NO_SPACE else hit.value
 
     def commit(self, req_id: int, num_computed: int) -> None:
@@ -224,7 +228,8 @@ SCHED_EXPORTED = ("pa_sched_create", "pa_sched_destroy", "pa_sched_add_request",
                   "pa_sched_plan", "pa_sched_plan_tokens", "pa_sched_plan_prefills",
                   "pa_sched_plan_max_blocks", "pa_sched_batch", "pa_sched_update",
                   "pa_sched_num_waiting", "pa_sched_num_running", "pa_sched_num_preemptions",
-                  "pa_sched_take_finished", "pa_sched_last_error", "pa_sched_num_swaps")
+                  "pa_sched_take_finished", "pa_sched_last_error", "pa_sched_num_swaps",
+                  "pa_sched_set_spec_tokens", "pa_sched_plan_drafts", "pa_sched_update_spec")
 
 
 class SchedConfig(ctypes.Structure):
@@ -249,6 +254,9 @@ def _load_sched(lib):
         "pa_sched_plan_max_blocks": (I32, [P]),
         "pa_sched_batch": (ctypes.c_int, [P, PI32, PI32, PI32, I32, I32, PI32, PI32]),
         "pa_sched_update": (I64, [P, PI32]),
+        "pa_sched_set_spec_tokens": (ctypes.c_int, [P, I64, PI32, I32]),
+        "pa_sched_plan_drafts": (ctypes.c_int, [P, PI32]),
+        "pa_sched_update_spec": (I64, [P, PI32, PI32]),
         "pa_sched_num_waiting": (I64, [P]),
         "pa_sched_num_running": (I64, [P]),
         "pa_sched_num_preemptions": (I64, [P]),
@@ -275,8 +283,10 @@ class StepBatch:
     """One step's plan and device-call metadata (numpy int32 arrays, batch order)."""
 
     def __init__(self, req_ids, starts, counts, num_prefills, query_start_loc, seq_lens,
-                 block_tables, slot_mapping, positions):
+                 block_tables, slot_mapping, positions, drafts=None):
         self.req_ids, self.starts, self.counts = req_ids, starts, counts
+        # draft tokens scheduled per request: the last drafts[i] of counts[i]
+        self.drafts = np.zeros_like(counts) if drafts is None else drafts
         self.num_prefills = num_prefills
         self.query_start_loc, self.seq_lens = query_start_loc, seq_lens
         self.block_tables, self.slot_mapping, self.positions = block_tables, slot_mapping, positions
@@ -332,6 +342,9 @@ class Scheduler:
         self._check(self._lib.pa_sched_plan(self._s, ids.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
                                             _p32(starts), _p32(counts)), "pa_sched_plan")
         ids, starts, counts = ids[:n], starts[:n], counts[:n]
+        drafts = np.zeros(max(n, 1), dtype=np.int32)
+        self._check(self._lib.pa_sched_plan_drafts(self._s, _p32(drafts)), "pa_sched_plan_drafts")
+        drafts = drafts[:n]
         p = self._check(self._lib.pa_sched_plan_prefills(self._s), "pa_sched_plan_prefills")
         tok = int(counts.sum())
         mb = max(self._lib.pa_sched_plan_max_blocks(self._s), 1)
@@ -342,11 +355,22 @@ class Scheduler:
         pos = np.zeros(max(tok, 1), dtype=np.int32)
         self._check(self._lib.pa_sched_batch(self._s, _p32(qsl), _p32(seq), _p32(tables), mb, pad_block,
                                              _p32(slots), _p32(pos)), "pa_sched_batch")
-        return StepBatch(ids, starts, counts, p, qsl, seq[:n], tables[:n], slots[:tok], pos[:tok])
+        return StepBatch(ids, starts, counts, p, qsl, seq[:n], tables[:n], slots[:tok], pos[:tok], drafts)
 
-    def update(self, sampled) -> int:
+    def set_spec_tokens(self, req_id, drafts) -> None:
+        """Draft tokens of a request for the next step (speculative decoding)."""
+        t = _i32(drafts) if len(drafts) else np.zeros(1, dtype=np.int32)
+        self._check(self._lib.pa_sched_set_spec_tokens(self._s, req_id, _p32(t), len(drafts)),
+                    "pa_sched_set_spec_tokens")
+
+    def update(self, sampled, accepted=None) -> int:
+        """sampled[i]: the token sampled for plan entry i; accepted[i]: how many of its
+        scheduled drafts were accepted (None: none)."""
         t = _i32(sampled) if len(sampled) else np.zeros(1, dtype=np.int32)
-        return self._check(self._lib.pa_sched_update(self._s, _p32(t)), "pa_sched_update")
+        if accepted is None:
+            return self._check(self._lib.pa_sched_update(self._s, _p32(t)), "pa_sched_update")
+        a = _i32(accepted) if len(accepted) else np.zeros(1, dtype=np.int32)
+        return self._check(self._lib.pa_sched_update_spec(self._s, _p32(t), _p32(a)), "pa_sched_update_spec")
 
     def num_waiting(self) -> int:
         return self._lib.pa_sched_num_waiting(self._s)

@@ -61,7 +61,8 @@ def random_session(seed, num_blocks, prefix, steps=150, num_host=0):
             else:
                 left = len(r.tokens) - r.computed - model.prefix_hit_tokens(rid)
                 n = rng.randint(0, max(left, 0))
-                got, want = lib.allocate_slots(rid, n), model.allocate_slots(rid, n)
+                look = rng.choice([0, 0, 0, 1, 3, 17])  # draft positions past the tokens
+                got, want = lib.allocate_slots(rid, n, look), model.allocate_slots(rid, n, look)
                 assert got == want
         elif op < 0.65:
             rid = rng.choice(live)

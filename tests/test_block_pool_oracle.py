@@ -65,6 +65,25 @@ def pin_new_request_takes_ceil_blocks():
         assert len(pool.free) == 8 - -(-n // B)
 
 
+def pin_lookahead_blocks_cover_the_drafts():
+    """Blocks for positions past the known tokens (speculative drafts): the table covers
+    them and their slots are addressable, but they never count as computed."""
+    pool = bp.BlockPoolModel(8, True)
+    pool.add_request(1, tokens(15))
+    assert pool.allocate_slots(1, 15, 2) == 0
+    assert len(pool.block_table(1)) == 2 and len(pool.slot_mapping(1, 15, 2)) == 2
+    pool.commit(1, 15)
+    with pytest.raises(ValueError):
+        pool.commit(1, 17)  # the drafts are not tokens of the request
+    pool.append_tokens(1, [3])
+    pool.commit(1, 16)      # an accepted draft becomes a computed token
+    assert pool.reqs[1].computed == 16 and pool.num_cached() == 1
+    free = list(pool.free)
+    assert pool.allocate_slots(1, 0, 16 * 7 + 1) is None  # 9 blocks in all: 7 more, 6 free
+    assert pool.free == free and len(pool.block_table(1)) == 2
+    assert pool.allocate_slots(1, 0, 16 * 7) == 0 and pool.free == []
+
+
 def pin_exhaustion_returns_none_and_changes_nothing():
     pool = bp.BlockPoolModel(4, True)
     pool.add_request(1, tokens(65))
@@ -259,7 +278,7 @@ ALL_PINS = [pin_swap_keeps_the_computed_tokens, pin_new_request_takes_ceil_block
             pin_extra_key_separates, pin_block_returns_only_at_zero_refs,
             pin_cached_blocks_evicted_last_prefix_last, pin_preempted_request_gets_its_prefix_back,
             pin_last_token_is_always_computed, pin_no_caching_when_disabled,
-            pin_reads_back_own_tokens_under_random_use]
+            pin_reads_back_own_tokens_under_random_use, pin_lookahead_blocks_cover_the_drafts]
 
 
 @pytest.mark.parametrize("pin", ALL_PINS, ids=lambda f: f.__name__)
@@ -267,9 +286,9 @@ def test_pin(pin):
     pin()
 
 
-def _partial_allocate(self, rid, n_new):
+def _partial_allocate(self, rid, n_new, lookahead=0):
     r = self.reqs[rid]
-    while len(r.blocks) < bp.ceil_blocks(r.computed + n_new) and self.free:
+    while len(r.blocks) < bp.ceil_blocks(r.computed + n_new + lookahead) and self.free:
         r.blocks.append(self.take_head())
     return 0
 
