@@ -83,7 +83,23 @@ def test_serving_short_prompts():
     assert runner.short_steps > 0
 
 
-def run_trace(num_blocks, budget, max_seqs, seed, num_host, prompt_len=(1, 120), heads=(0, 16, 33, 40)):
+@pytest.mark.parametrize("num_blocks,budget,max_seqs,seed,num_host",
+                         [(200, 64, 8, 7, 0), (40, 96, 8, 8, 0), (24, 48, 6, 9, 10)])
+def test_serving_speculative_drafts(num_blocks, budget, max_seqs, seed, num_host):
+    """Speculative decoding: before every step each request gets 0-3 draft tokens; a running
+    request that has caught up computes them after its newest token (its chunk then has up
+    to 4 rows, the short-chunk call's limit for 4 q heads per kv head), the draft rows must
+    match the oracle's causal attention over the pool, and a random number of them is
+    accepted. Rejected drafts leave K/V in slots past the computed tokens, and the pool
+    must still equal the oracle's mirror at the end."""
+    say(f"serving trace with drafts: blocks {num_blocks}, budget {budget}, seed {seed}, swap space {num_host}")
+    runner = run_trace(num_blocks, budget, max_seqs, seed, num_host, spec=True)
+    say(f"  {runner.short_steps} steps through the short-chunk call")
+    assert runner.short_steps > 0
+
+
+def run_trace(num_blocks, budget, max_seqs, seed, num_host, prompt_len=(1, 120), heads=(0, 16, 33, 40),
+              spec=False):
     rng = np.random.default_rng(seed)
     synth = Synth(seed)
     pool = host.BlockPool(num_blocks, True, num_host)
@@ -113,12 +129,21 @@ def run_trace(num_blocks, budget, max_seqs, seed, num_host, prompt_len=(1, 120),
     scale = 1 / np.sqrt(D)
     mx, rel = TOL["bf16"]
     steps = 0
+    finished = set()
+    drafted = 0
     while sched.num_waiting() or sched.num_running():
+        drafts = {}
+        if spec:  # draft tokens for every unfinished request; only caught-up running ones use them
+            for r in tokens:
+                if r not in finished:
+                    drafts[r] = rng.integers(0, 500, int(rng.integers(0, 4))).tolist()
+                    sched.set_spec_tokens(r, drafts[r])
         b = sched.schedule()
         assert b.num_seqs > 0, "scheduler stalled"
         ops = pool.take_ops()
-        parts = [synth.rows(tokens[int(r)], salts[int(r)], int(a), int(c))
-                 for r, a, c in zip(b.req_ids, b.starts, b.counts)]
+        parts = [synth.rows(tokens[int(r)] + drafts.get(int(r), [])[:int(d)], salts[int(r)], int(a), int(c))
+                 for r, a, c, d in zip(b.req_ids, b.starts, b.counts, b.drafts)]
+        drafted += int(b.drafts.sum())
         key = np.concatenate([p[0] for p in parts])
         value = np.concatenate([p[1] for p in parts])
         q = np.concatenate([p[2] for p in parts])
@@ -145,15 +170,20 @@ def run_trace(num_blocks, budget, max_seqs, seed, num_host, prompt_len=(1, 120),
             assert_close(got[n_pf:], ref, "bf16", f"step {steps} decode ({b.num_seqs - P} requests)")
 
         sampled = rng.integers(0, 500, b.num_seqs)
-        sched.update(sampled)
+        accepted = [int(rng.integers(0, d + 1)) for d in b.drafts] if spec else None
+        sched.update(sampled, accepted)
         done = set(sched.take_finished())
-        for i, (r, a, c) in enumerate(zip(b.req_ids, b.starts, b.counts)):
+        finished |= done
+        for i, (r, a, c, d) in enumerate(zip(b.req_ids, b.starts, b.counts, b.drafts)):
             r = int(r)
-            if a + c == len(tokens[r]) and r not in done:
-                tokens[r].append(int(sampled[i]))
+            if a + c - d == len(tokens[r]) and r not in done:
+                tokens[r] += drafts.get(r, [])[:accepted[i] if spec else 0] + [int(sampled[i])]
         steps += 1
         assert steps < 2000
-    say(f"  {steps} steps, {sched.num_preemptions()} preemptions, {sched.num_swaps()} by swapping")
+    say(f"  {steps} steps, {sched.num_preemptions()} preemptions, {sched.num_swaps()} by swapping, "
+        f"{drafted} draft tokens")
+    if spec:
+        assert drafted > 0
     assert np.array_equal(host_bits(k_gpu), k_host) and np.array_equal(host_bits(v_gpu), v_host)
     sk = swap_k.view(torch.int16).numpy().view(np.uint16)
     sv = swap_v.view(torch.int16).numpy().view(np.uint16)
