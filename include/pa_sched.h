@@ -98,6 +98,11 @@ int pa_sched_add_request(pa_scheduler* sched, int64_t req_id, const int32_t* pro
 /* Draft tokens [num_drafts >= 0] of a queued request for the next step
  * (replacing any set before); dropped at the next pa_sched_update. */
 int pa_sched_set_spec_tokens(pa_scheduler* sched, int64_t req_id, const int32_t* drafts, int32_t num_drafts);
+/* The same for num_requests requests at once: request req_ids[i] gets
+ * drafts[offsets[i] .. offsets[i+1]-1] (offsets [num_requests + 1], starting at
+ * 0, non-decreasing). Checked in full before anything changes. */
+int pa_sched_set_spec_tokens_batch(pa_scheduler* sched, int64_t num_requests, const int64_t* req_ids,
+                                   const int64_t* offsets, const int32_t* drafts);
 
 /* Plan the next step; returns the number of scheduled requests or an error.
  * The plan stays readable until the next pa_sched_schedule. */

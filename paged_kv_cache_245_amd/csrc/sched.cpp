@@ -125,6 +125,20 @@ int pa_sched_set_spec_tokens(pa_scheduler* s, int64_t req_id, const int32_t* dra
   return PA_POOL_OK;
 }
 
+int pa_sched_set_spec_tokens_batch(pa_scheduler* s, int64_t num_requests, const int64_t* req_ids,
+                                   const int64_t* offsets, const int32_t* drafts) {
+  if (s == nullptr || num_requests < 0 || (num_requests > 0 && (req_ids == nullptr || offsets == nullptr)))
+    return fail(PA_POOL_ERR_INVALID_ARG, "null pointer");
+  for (int64_t i = 0; i < num_requests; ++i) {  // check everything before changing anything
+    if (s->reqs.count(req_ids[i]) == 0) return fail(PA_POOL_ERR_INVALID_ARG, "unknown request");
+    if (offsets[i + 1] < offsets[i] || offsets[0] != 0 || (offsets[i + 1] > 0 && drafts == nullptr))
+      return fail(PA_POOL_ERR_INVALID_ARG, "offsets must start at 0 and not decrease");
+  }
+  for (int64_t i = 0; i < num_requests; ++i)
+    s->drafts[req_ids[i]].assign(drafts + offsets[i], drafts + offsets[i + 1]);
+  return PA_POOL_OK;
+}
+
 int64_t pa_sched_schedule(pa_scheduler* s) {
   if (s == nullptr) return fail(PA_POOL_ERR_INVALID_ARG, "null scheduler");
   std::vector<Item> order;  // scheduling order

@@ -229,7 +229,8 @@ SCHED_EXPORTED = ("pa_sched_create", "pa_sched_destroy", "pa_sched_add_request",
                   "pa_sched_plan_max_blocks", "pa_sched_batch", "pa_sched_update",
                   "pa_sched_num_waiting", "pa_sched_num_running", "pa_sched_num_preemptions",
                   "pa_sched_take_finished", "pa_sched_last_error", "pa_sched_num_swaps",
-                  "pa_sched_set_spec_tokens", "pa_sched_plan_drafts", "pa_sched_update_spec")
+                  "pa_sched_set_spec_tokens", "pa_sched_set_spec_tokens_batch", "pa_sched_plan_drafts",
+                  "pa_sched_update_spec")
 
 
 class SchedConfig(ctypes.Structure):
@@ -255,6 +256,7 @@ def _load_sched(lib):
         "pa_sched_batch": (ctypes.c_int, [P, PI32, PI32, PI32, I32, I32, PI32, PI32]),
         "pa_sched_update": (I64, [P, PI32]),
         "pa_sched_set_spec_tokens": (ctypes.c_int, [P, I64, PI32, I32]),
+        "pa_sched_set_spec_tokens_batch": (ctypes.c_int, [P, I64, PI64, PI64, PI32]),
         "pa_sched_plan_drafts": (ctypes.c_int, [P, PI32]),
         "pa_sched_update_spec": (I64, [P, PI32, PI32]),
         "pa_sched_num_waiting": (I64, [P]),
@@ -362,6 +364,19 @@ class Scheduler:
         t = _i32(drafts) if len(drafts) else np.zeros(1, dtype=np.int32)
         self._check(self._lib.pa_sched_set_spec_tokens(self._s, req_id, _p32(t), len(drafts)),
                     "pa_sched_set_spec_tokens")
+
+    def set_spec_tokens_batch(self, req_ids, drafts) -> None:
+        """Draft tokens for several requests in one call: drafts[i] for req_ids[i]."""
+        ids = np.ascontiguousarray(req_ids, dtype=np.int64)
+        lens = np.array([len(d) for d in drafts], dtype=np.int64)
+        offsets = np.zeros(len(ids) + 1, dtype=np.int64)
+        np.cumsum(lens, out=offsets[1:])
+        flat = np.ascontiguousarray(np.concatenate([np.asarray(d, dtype=np.int32) for d in drafts])
+                                    if len(drafts) and offsets[-1] else np.zeros(1, dtype=np.int32))
+        P64 = ctypes.POINTER(ctypes.c_int64)
+        self._check(self._lib.pa_sched_set_spec_tokens_batch(self._s, len(ids), ids.ctypes.data_as(P64),
+                                                             offsets.ctypes.data_as(P64), _p32(flat)),
+                    "pa_sched_set_spec_tokens_batch")
 
     def update(self, sampled, accepted=None) -> int:
         """sampled[i]: the token sampled for plan entry i; accepted[i]: how many of its

@@ -130,6 +130,43 @@ def test_draft_arguments_are_checked():
     assert s.pool.request_tokens(1) == 6 and s.pool.request_computed(1) == 5
 
 
+def test_batched_drafts_equal_one_by_one():
+    """pa_sched_set_spec_tokens_batch plans the same steps as one call per request, and a
+    bad entry changes nothing."""
+    plans = []
+    for batched in (False, True):
+        pool = host.BlockPool(64)
+        s = host.Scheduler(pool, 40, 8)
+        for i in range(5):
+            s.add_request(i, list(range(10 + 3 * i)), 6)
+        rng = random.Random(5)
+        seen = []
+        while s.num_waiting() or s.num_running():
+            live = [i for i in range(5) if i not in done_ids(seen)]
+            drafts = [[rng.randint(0, 9) for _ in range(rng.randint(0, 3))] for _ in live]
+            if batched:
+                s.set_spec_tokens_batch(live, drafts)
+            else:
+                for r, d in zip(live, drafts):
+                    s.set_spec_tokens(r, d)
+            b = s.schedule()
+            seen.append((b.req_ids.tolist(), b.counts.tolist(), b.drafts.tolist()))
+            s.update([1] * b.num_seqs, [min(1, int(d)) for d in b.drafts])
+            seen[-1] += (s.take_finished(),)
+        plans.append(seen)
+    assert plans[0] == plans[1]
+    s = host.Scheduler(host.BlockPool(8), 16, 4)
+    s.add_request(1, [1, 2], 3)
+    with pytest.raises(host.SchedError):
+        s.set_spec_tokens_batch([1, 9], [[4], [5]])  # request 9 is unknown
+    b = s.schedule()
+    assert b.drafts.tolist() == [0]  # nothing was set
+
+
+def done_ids(seen):
+    return {r for step in seen for r in step[3]}
+
+
 def test_exported_symbols():
     lib = host.load_host()
     for name in host.SCHED_EXPORTED:
