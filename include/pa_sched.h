@@ -49,9 +49,11 @@
  * The step's batch is laid out for one pa_write_kv and one pa_prefill_chunk (the
  * requests given more than one token) and one pa_decode_append (those given
  * one, whose new token is the newest of their context):
- * scheduled requests in batch order are the multi-token ones, then the
- * one-token ones, each group in scheduling order; new tokens are packed in the
- * same order. The block operations the step caused (swap-outs, swap-ins,
+ * scheduled requests in batch order are the multi-token ones, the longest
+ * first (ties in scheduling order), then the one-token ones in scheduling
+ * order; new tokens are packed in the same order. Short chunks (such as a
+ * request's drafts) thus end the multi-token group, where a caller can hand
+ * them to pa_prefill_chunk_short and the rest to pa_prefill_chunk. The block operations the step caused (swap-outs, swap-ins,
  * copy-on-write copies) are taken from the pool with pa_pool_take_ops and run,
  * in order, before the step's pa_write_kv.
  *

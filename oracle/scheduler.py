@@ -28,7 +28,9 @@ waiting request whose remaining tokens exceed the budget left; under priority
 scheduling the waiting queue is kept in (priority, arrival) order and a victim
 already scheduled in the step is taken out of it; a request finishes on its
 max_new_tokens-th generated token, which is not appended; the batch lists the
-requests given more than one token first, then the one-token ones; in swap mode
+requests given more than one token first, the longest first, then the one-token
+ones (short chunks, such as a request's drafts, then sit together at the end of
+the multi-token group); in swap mode
 the victim is swapped out when the swap space has room (else recomputed), and a
 swapped request is admitted only when the free queue covers its swap-in and the
 blocks of the tokens it is given, resuming at its computed count. Drafts: they
@@ -178,7 +180,9 @@ class SchedulerModel:
             self.running.append(rid)
             order.append((rid, hit, n))
             budget -= n
-        self.plan = [x for x in order if x[2] > 1] + [x for x in order if x[2] == 1]
+        # multi-token requests first, the longest first (ties in scheduling order), then
+        # the one-token ones in scheduling order
+        self.plan = sorted([x for x in order if x[2] > 1], key=lambda x: -x[2]) + [x for x in order if x[2] == 1]
         self.plan_drafts = [look.get(x[0], 0) for x in self.plan]
         return list(self.plan)
 

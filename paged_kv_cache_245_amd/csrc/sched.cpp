@@ -234,6 +234,9 @@ int64_t pa_sched_schedule(pa_scheduler* s) {
   s->plan.clear();
   for (const Item& x : order)
     if (x.count > 1) s->plan.push_back(x);
+  // the multi-token requests longest first (ties keep scheduling order), so that
+  // short chunks (a request's drafts) end the group and can go to another call
+  std::stable_sort(s->plan.begin(), s->plan.end(), [](const Item& a, const Item& b) { return a.count > b.count; });
   for (const Item& x : order)
     if (x.count == 1) s->plan.push_back(x);
   return (int64_t)s->plan.size();

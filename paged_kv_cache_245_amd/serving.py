@@ -17,12 +17,14 @@ wavefronts fit beside the prefill's on every compute unit: the prefill keeps
 the matrix cores busy while the decode streams K/V from HBM. The two calls
 touch disjoint memory (the decode stores only into each one-token request's
 own last block; blocks shared with other requests are full and never
-written). A step whose chunks are all short (at most 16 / (q heads per kv
-head) tokens, as when every request scores a few tokens at once) runs them
-through pa_prefill_chunk_short instead, on the caller's stream, followed by
-the decode: both calls then stream K/V from HBM, and running them side by side
-gains nothing. Marshalling and sequencing only; the work runs in libpa.so's
-kernels.
+written). Short chunks (at most 16 / (q heads per kv head) tokens, as when a
+request scores its draft tokens) go through pa_prefill_chunk_short: the
+scheduler lists the multi-token requests longest first, so the short ones end
+the group, and the call takes them after the pa_prefill_chunk of the rest, on
+the caller's stream. A step whose chunks are all short runs that call and then
+the decode on the caller's stream: both stream K/V from HBM, and running them
+side by side gains nothing. Marshalling and sequencing only; the work runs in
+libpa.so's kernels.
 """
 from __future__ import annotations
 
@@ -72,8 +74,9 @@ class StepRunner:
         self.host_k, self.host_v = host_k, host_v
         self.max_seqs, self.max_tokens, self.max_blocks = max_seqs, max_tokens, max_blocks_per_seq
         self.device = torch.device(device)
-        # room for one step's metadata (int32): qsl | seq_lens | tables | slots
-        self.n_meta = (max_seqs + 1) + max_seqs + max_seqs * max_blocks_per_seq + max_tokens
+        # room for one step's metadata (int32): qsl | seq_lens | tables | slots | the short
+        # chunks' own qsl
+        self.n_meta = (max_seqs + 1) + max_seqs + max_seqs * max_blocks_per_seq + max_tokens + (max_seqs + 1)
         self.host = [torch.empty(self.n_meta, dtype=torch.int32, pin_memory=True) for _ in range(2)]
         self.done = [None, None]
         self.turn = 0
@@ -83,7 +86,8 @@ class StepRunner:
         # steps of short chunks: pa_prefill_chunk_short and its own workspace
         self.short_rows = 0
         self.ws_short = None
-        self.short_steps = 0  # steps whose chunks went through pa_prefill_chunk_short
+        self.short_steps = 0  # steps with chunks through pa_prefill_chunk_short
+        self.split_steps = 0  # of them, steps that also had longer chunks
         if desc.dtype == pa.PA_BF16 and max_seqs <= 8192:
             self.short_rows = pa.pa_prefill_chunk_short_max_query_len(desc)
             self.ws_short = pa.chunk_short_workspace(desc, max_seqs, self.short_rows, self.device)
@@ -128,6 +132,21 @@ class StepRunner:
         h[o_seq:o_tab] = batch.seq_lens
         h[o_tab:o_slot] = batch.block_tables.reshape(-1)
         h[o_slot:end] = batch.slot_mapping
+        # multi-token requests come longest first (the scheduler's order): those from j on
+        # are short chunks. A batch in another order goes through pa_prefill_chunk whole
+        # unless every chunk is short.
+        counts = batch.counts[:P]
+        short_mask = counts <= self.short_rows
+        if P and short_mask.all():
+            j = 0
+        elif P and short_mask[-1] and np.all(np.diff(counts) <= 0):
+            j = int(np.argmax(short_mask))
+        else:
+            j = P
+        o_short = end
+        if j < P:  # their row offsets, from 0 at their first row
+            end = o_short + (P - j) + 1
+            h[o_short:end] = batch.query_start_loc[j:] - batch.query_start_loc[j]
         self.meta[:end].copy_(buf[:end], non_blocking=True)
         ev = torch.cuda.Event()
         ev.record(stream)
@@ -137,27 +156,30 @@ class StepRunner:
         qsl = self.meta[:o_seq]
         seq = self.meta[o_seq:o_tab]
         tables = self.meta[o_tab:o_slot].view(S, mb)
-        slots = self.meta[o_slot:end]
+        slots = self.meta[o_slot:o_short]
         n_pf = int(batch.query_start_loc[-1])
         if S > P:
             need = pa.pa_decode_workspace_size(self.desc, S - P, int(batch.seq_lens[P:].max()))
             if need > self.ws_bytes:
                 raise ValueError("decode workspace too small for this step")
-        longest = int(batch.counts[:P].max()) if P else 0
-        short = P > 0 and longest <= self.short_rows
+        short = P > 0 and j == 0  # every chunk short
         fork = P > 0 and S > P and not short
         if P:
             pa.pa_write_kv(self.desc, key[:n_pf], value[:n_pf], self.k, self.v, slots[:n_pf])
             if fork:
                 self.side.wait_stream(stream)
-            if short:
+            if j > 0:  # the longer chunks on the matrix cores
+                r = int(batch.query_start_loc[j])
+                pa.pa_prefill_chunk(self.desc, out[:r], q[:r], self.k, self.v, qsl[:j + 1], seq[:j], tables[:j],
+                                    int(counts[0]), int(batch.seq_lens[:j].max()), self.scale)
+            if j < P:  # the short ones through the decode kernel
+                r = int(batch.query_start_loc[j])
                 self.short_steps += 1
-                pa.pa_prefill_chunk_short(self.desc, out[:n_pf], q[:n_pf], self.k, self.v, qsl, seq[:P],
-                                          tables[:P], longest, int(batch.seq_lens[:P].max()), self.scale,
+                self.split_steps += j > 0
+                pa.pa_prefill_chunk_short(self.desc, out[r:n_pf], q[r:n_pf], self.k, self.v,
+                                          self.meta[o_short:o_short + P - j + 1], seq[j:P], tables[j:P],
+                                          int(counts[j]), int(batch.seq_lens[j:P].max()), self.scale,
                                           self.ws_short)
-            else:
-                pa.pa_prefill_chunk(self.desc, out[:n_pf], q[:n_pf], self.k, self.v, qsl, seq[:P], tables[:P],
-                                    longest, int(batch.seq_lens[:P].max()), self.scale)
         if S > P:
             # a one-token request's new token is its newest, at position seq_len - 1
             args = (self.desc, out[n_pf:N], q[n_pf:N], key[n_pf:N], value[n_pf:N], self.k, self.v,

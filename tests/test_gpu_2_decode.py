@@ -50,6 +50,24 @@ def same_pools(k, v, ok, ov):
 
 
 @pytest.mark.timeout(600)
+def test_long_context_short_chunk_all_rows(long_context):
+    """pa_prefill_chunk_short with one-row chunks over the 131,072-token contexts (a decode
+    is a chunk of one row): every (request, q head) row against the oracle's decode."""
+    w, ok, ov, ref = long_context
+    say("  config 5 through pa_prefill_chunk_short, one-row chunks, all rows")
+    d, k, v = gpu_pools(w)
+    dec = w.decode
+    S = len(dec.context_lens)
+    q = device_tensor(dec.q, "bf16")
+    out = torch.empty_like(q)
+    ws = pa.chunk_short_workspace(d, S, 1)
+    pa.pa_prefill_chunk_short(d, out, q, k, v, i32(np.arange(S + 1)), i32(dec.context_lens),
+                              i32(dec.block_tables), 1, dec.max_context_len, w.scale, ws)
+    torch.cuda.synchronize()
+    assert_close(as64(out), ref, "bf16", "config 5, pa_prefill_chunk_short, all 512 rows")
+
+
+@pytest.mark.timeout(600)
 def test_long_context_decode_all_rows(long_context):
     """pa_decode over 131,072-token contexts: every (request, q head) row against the oracle."""
     w, ok, ov, ref = long_context

@@ -84,18 +84,21 @@ def test_serving_short_prompts():
 
 
 @pytest.mark.parametrize("num_blocks,budget,max_seqs,seed,num_host",
-                         [(200, 64, 8, 7, 0), (40, 96, 8, 8, 0), (24, 48, 6, 9, 10)])
+                         [(200, 64, 8, 7, 0), (32, 96, 8, 8, 0), (24, 48, 6, 9, 10)])
 def test_serving_speculative_drafts(num_blocks, budget, max_seqs, seed, num_host):
     """Speculative decoding: before every step each request gets 0-3 draft tokens; a running
     request that has caught up computes them after its newest token (its chunk then has up
     to 4 rows, the short-chunk call's limit for 4 q heads per kv head), the draft rows must
     match the oracle's causal attention over the pool, and a random number of them is
     accepted. Rejected drafts leave K/V in slots past the computed tokens, and the pool
-    must still equal the oracle's mirror at the end."""
+    must still equal the oracle's mirror at the end. In steps that also admit prompts,
+    the longer chunks go through pa_prefill_chunk and the draft rows through the
+    short-chunk call."""
     say(f"serving trace with drafts: blocks {num_blocks}, budget {budget}, seed {seed}, swap space {num_host}")
     runner = run_trace(num_blocks, budget, max_seqs, seed, num_host, spec=True)
-    say(f"  {runner.short_steps} steps through the short-chunk call")
-    assert runner.short_steps > 0
+    say(f"  {runner.short_steps} steps through the short-chunk call, {runner.split_steps} of them beside "
+        f"pa_prefill_chunk")
+    assert runner.short_steps > 0 and runner.split_steps > 0
 
 
 def run_trace(num_blocks, budget, max_seqs, seed, num_host, prompt_len=(1, 120), heads=(0, 16, 33, 40),
