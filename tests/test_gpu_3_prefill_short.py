@@ -106,6 +106,24 @@ def test_positions_beyond_chunks():
     check(w, "positions beyond the chunks", max_query_len=4)
 
 
+@pytest.mark.parametrize("seed", range(530, 538))
+def test_random_sweep(seed):
+    """Random group sizes, head dims, batch sizes, chunk lengths (up to the limit) and
+    contexts (some ending inside a block, some a few thousand tokens long)."""
+    rng = np.random.default_rng(seed)
+    group = int(rng.choice([1, 2, 4, 8, 16]))
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    D = int(rng.choice([64, 128]))
+    S = int(rng.integers(1, 40))
+    n_max = 16 // group
+    new = rng.integers(1, n_max + 1, S)
+    cached = np.where(rng.random(S) < 0.3, rng.integers(0, 40, S), rng.integers(0, 3000, S))
+    say(f"  random short chunks: seed {seed}, G={group}, Hkv={hkv}, D={D}, S={S}")
+    w = workloads.custom_prefill(seed, cached=cached.tolist(), new=new.tolist(), Hq=group * hkv, Hkv=hkv, D=D,
+                                 dtype="bf16")
+    check(w, f"random sweep seed {seed}")
+
+
 def test_empty_chunk_is_skipped():
     w = workloads.custom_prefill(515, cached=[3, 900], new=[2, 3], Hq=8, Hkv=2, D=64, dtype="bf16")
     d, k, v = gpu_pools(w)
