@@ -13,6 +13,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import paged_kv_cache_245_amd as pa
 import workloads
 from gpu_support import as64, assert_close, device_tensor, gpu_pools, i32, say
@@ -183,6 +184,48 @@ def test_shared_prefix_call_replayed_matches_eager():
         torch.cuda.synchronize()
     ok, ov = oracle_pools(w)
     assert_close(as64(out_g), oracle_decode(w, ok, ov), "bf16", "shared prefix, graph-replayed")
+
+
+def test_short_chunk_call_replayed_matches_eager():
+    """pa_prefill_chunk_short (chunk kernel and merge; whole requests written through LDS
+    records, split ones through the merge) captured in a HIP graph and replayed gives the
+    eager call's output bit for bit, replay after replay, and the oracle's."""
+    say("  short-chunk call replayed from a graph")
+    rng = np.random.default_rng(32)
+    cached = rng.integers(0, 3000, 48)
+    w = workloads.custom_prefill(32, cached=cached.tolist(), new=rng.integers(1, 5, 48).tolist(), Hq=32, Hkv=8,
+                                 D=128, dtype="bf16")
+    d, k, v = gpu_pools(w)
+    p = w.prefill
+    q = device_tensor(p.q, "bf16")
+    qsl, seq, tables = i32(p.query_start_loc), i32(p.seq_lens), i32(p.block_tables)
+    ws = pa.chunk_short_workspace(d, 48, 4)
+    out_e, out_g = torch.empty_like(q), torch.empty_like(q)
+
+    def call(out):
+        pa.pa_prefill_chunk_short(d, out, q, k, v, qsl, seq, tables, 4, p.max_seq_len, w.scale, ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(out_e)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    eager = bits(out_e)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(out_g)
+    for rep in range(3):
+        out_g.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(out_g), eager), f"replay {rep}"
+        call(out_e)  # eager work between the replays
+        torch.cuda.synchronize()
+    ok, ov = oracle_pools(w)
+    ref = oracle.prefill_chunk(p.q, ok, ov, p.query_start_loc, p.seq_lens, p.block_tables, "bf16", w.scale)
+    assert_close(as64(out_g), ref, "bf16", "short chunks, graph-replayed")
 
 
 def test_first_decode_call_inside_capture():
