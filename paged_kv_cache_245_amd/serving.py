@@ -55,6 +55,20 @@ def batch_ops(ops):
     return [(kind, pairs) for kind, pairs, _, _ in runs]
 
 
+def short_tail_start(counts, short_rows):
+    """Index of the first multi-token request whose chunk goes to pa_prefill_chunk_short:
+    0 when every chunk has at most short_rows rows, the start of the short tail when the
+    counts come longest first (the scheduler's order), else len(counts) (none)."""
+    counts = np.asarray(counts)
+    P = len(counts)
+    short = counts <= short_rows
+    if P and short.all():
+        return 0
+    if P and short[-1] and np.all(np.diff(counts) <= 0):
+        return int(np.argmax(short))
+    return P
+
+
 class StepRunner:
     """Device buffers for the steps of one pool: metadata staging and the decode workspace.
 
@@ -136,13 +150,7 @@ class StepRunner:
         # are short chunks. A batch in another order goes through pa_prefill_chunk whole
         # unless every chunk is short.
         counts = batch.counts[:P]
-        short_mask = counts <= self.short_rows
-        if P and short_mask.all():
-            j = 0
-        elif P and short_mask[-1] and np.all(np.diff(counts) <= 0):
-            j = int(np.argmax(short_mask))
-        else:
-            j = P
+        j = short_tail_start(counts, self.short_rows)
         o_short = end
         if j < P:  # their row offsets, from 0 at their first row
             end = o_short + (P - j) + 1
