@@ -366,13 +366,21 @@ class Scheduler:
                     "pa_sched_set_spec_tokens")
 
     def set_spec_tokens_batch(self, req_ids, drafts) -> None:
-        """Draft tokens for several requests in one call: drafts[i] for req_ids[i]."""
+        """Draft tokens for several requests in one call: drafts[i] for req_ids[i]; drafts is a
+        list of sequences, or a 2-D array when every request gets the same number."""
         ids = np.ascontiguousarray(req_ids, dtype=np.int64)
-        lens = np.array([len(d) for d in drafts], dtype=np.int64)
-        offsets = np.zeros(len(ids) + 1, dtype=np.int64)
-        np.cumsum(lens, out=offsets[1:])
-        flat = np.ascontiguousarray(np.concatenate([np.asarray(d, dtype=np.int32) for d in drafts])
-                                    if len(drafts) and offsets[-1] else np.zeros(1, dtype=np.int32))
+        if isinstance(drafts, np.ndarray) and drafts.ndim == 2:
+            offsets = np.arange(len(ids) + 1, dtype=np.int64) * drafts.shape[1]
+            flat = np.ascontiguousarray(drafts, dtype=np.int32).reshape(-1)
+        else:
+            lens = np.array([len(d) for d in drafts], dtype=np.int64)
+            offsets = np.zeros(len(ids) + 1, dtype=np.int64)
+            np.cumsum(lens, out=offsets[1:])
+            flat = (np.concatenate([np.asarray(d, dtype=np.int32) for d in drafts])
+                    if len(drafts) and offsets[-1] else np.zeros(0, dtype=np.int32))
+        if flat.size == 0:
+            flat = np.zeros(1, dtype=np.int32)
+        flat = np.ascontiguousarray(flat, dtype=np.int32)
         P64 = ctypes.POINTER(ctypes.c_int64)
         self._check(self._lib.pa_sched_set_spec_tokens_batch(self._s, len(ids), ids.ctypes.data_as(P64),
                                                              offsets.ctypes.data_as(P64), _p32(flat)),

@@ -155,6 +155,19 @@ def test_batched_drafts_equal_one_by_one():
             seen[-1] += (s.take_finished(),)
         plans.append(seen)
     assert plans[0] == plans[1]
+    # a 2-D array (the same number of drafts for every request) plans the same as lists
+    steps = []
+    for as_array in (False, True):
+        s = host.Scheduler(host.BlockPool(64), 64, 8)
+        for i in range(3):
+            s.add_request(i, [1, 2, 3 + i], 5)
+        s.schedule()
+        s.update([7, 8, 9])
+        d = np.array([[11, 12], [13, 14], [15, 16]], dtype=np.int32)
+        s.set_spec_tokens_batch([0, 1, 2], d if as_array else d.tolist())
+        b = s.schedule()
+        steps.append((b.req_ids.tolist(), b.counts.tolist(), b.drafts.tolist()))
+    assert steps[0] == steps[1] and steps[0][2] == [2, 2, 2]
     s = host.Scheduler(host.BlockPool(8), 16, 4)
     s.add_request(1, [1, 2], 3)
     with pytest.raises(host.SchedError):
