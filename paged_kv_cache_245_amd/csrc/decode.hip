@@ -1155,6 +1155,100 @@ __global__ __launch_bounds__(64 * kMergeHeads) void decode_merge_chunk_kernel(De
   }
 }
 
+// Short-chunk mode merge for requests split over many workers (more than eight
+// partials each on average): one wavefront per (q head, request, position) whose
+// four 16-lane groups fold every fourth partial each, so the chain of rounds of
+// eight loads is a quarter as long; the groups' results are combined across lanes
+// (each lane holds D/16 dims). A group may meet only partials without a key (its
+// workers lie past the position's causal limit): its maximum is then taken as 0
+// in the exponentials, and it contributes nothing.
+template <int D>
+__global__ __launch_bounds__(64 * kMergeHeads) void decode_merge_chunk_split_kernel(DecodeArgs a) {
+  constexpr int kE = D / 16;   // dims per lane
+  constexpr int kBatch = 8;    // partials per group and round, all loads issued first
+  const int lane = threadIdx.x & 63;
+  const int grp = lane >> 4, dl = lane & 15;
+  const int h = blockIdx.y * kMergeHeads + (threadIdx.x >> 6);
+  if (h >= a.num_q_heads) return;  // whole wavefront; the kernel has no barrier
+  const int s = blockIdx.x / a.n_cols, p = blockIdx.x % a.n_cols;  // grid x: (request, position)
+  const int q0 = a.query_start_loc[s], nq = a.query_start_loc[s + 1] - q0;
+  const int L = min(a.context_lens[s], a.max_context_len);
+  const int64_t T = a.cum_blocks[a.num_seqs];
+  const int64_t c0 = a.cum_blocks[s], c1 = a.cum_blocks[s + 1];
+  if (p >= nq || L <= 0) return;  // whole wavefront: no such position
+  const int64_t Tn = max(T, (int64_t)1);
+  const int W = (int)min((int64_t)a.num_workers, Tn);  // as in the decode kernel
+  const int w0 = worker_of(c0, Tn, W);
+  const int w1 = worker_of(max(c1 - 1, c0), Tn, W);
+  if (w0 == w1) return;  // one segment: written by the decode kernel
+  const int np = w1 - w0 + 1;
+  const int64_t rstep = (int64_t)a.n_cols * a.num_q_heads;
+  const int64_t row0 = ((int64_t)s + w0) * rstep + (int64_t)p * a.num_q_heads + h;
+  float M = -INFINITY, den = 0.f, o[kE];
+#pragma unroll
+  for (int e = 0; e < kE; ++e) o[e] = 0.f;
+  for (int i0 = grp; i0 < np; i0 += 4 * kBatch) {
+    float mi[kBatch], li[kBatch], ai[kBatch][kE];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int i = i0 + 4 * j;
+      const bool in = i < np;
+      const int64_t r = row0 + (in ? i : 0) * rstep;
+      mi[j] = in ? a.part_ml[2 * r] : -INFINITY;
+      li[j] = in ? a.part_ml[2 * r + 1] : 0.f;
+      const float* src = a.part_acc + r * D + dl * kE;
+#pragma unroll
+      for (int v = 0; v < kE / 4; ++v) {
+        const f32x4 x = in ? *(const f32x4*)(src + 4 * v) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) ai[j][4 * v + t] = x[t];
+      }
+    }
+    float mb = M;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) mb = fmaxf(mb, mi[j]);
+    const float mb_use = mb == -INFINITY ? 0.f : mb;
+    const float alpha = fast_exp2(M - mb_use);
+    den *= alpha;
+#pragma unroll
+    for (int e = 0; e < kE; ++e) o[e] *= alpha;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const float wgt = fast_exp2(mi[j] - mb_use);  // 0 for padding and empty partials
+      den += wgt * li[j];
+#pragma unroll
+      for (int e = 0; e < kE; ++e) o[e] += wgt * ai[j][e];
+    }
+    M = mb;
+  }
+  // combine the four groups: lanes 16 and 32 apart hold the same dims
+#pragma unroll
+  for (int off = 16; off <= 32; off <<= 1) {
+    const float M2 = __shfl_xor(M, off, 64);
+    const float den2 = __shfl_xor(den, off, 64);
+    float o2[kE];
+#pragma unroll
+    for (int e = 0; e < kE; ++e) o2[e] = __shfl_xor(o[e], off, 64);
+    const float Mn = fmaxf(M, M2);
+    const float Mn_use = Mn == -INFINITY ? 0.f : Mn;  // both empty: stay empty
+    const float w1 = fast_exp2(M - Mn_use), w2 = fast_exp2(M2 - Mn_use);
+    den = den * w1 + den2 * w2;
+#pragma unroll
+    for (int e = 0; e < kE; ++e) o[e] = o[e] * w1 + o2[e] * w2;
+    M = Mn;
+  }
+  if (grp != 0) return;  // every group holds the result; group 0 stores it
+  const float inv = 1.f / den;  // partial 0 holds key 0, which every position attends
+  uint16_t* O = (uint16_t*)a.out + ((int64_t)(q0 + p) * a.num_q_heads + h) * D + dl * kE;
+  if constexpr (kE == 4) {
+    *(u32x2*)O = u32x2{pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv)};
+  } else {
+    static_assert(kE == 8, "dims per lane");
+    *(u32x4*)O = u32x4{pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv),
+                       pack_bf16x2(o[4] * inv, o[5] * inv), pack_bf16x2(o[6] * inv, o[7] * inv)};
+  }
+}
+
 // Balanced mode merge for requests split over many workers (many partials each):
 // kWideThreads threads per (q head, request). Groups of D/4 threads own 4 dims
 // each; group g folds partials g, g + kG, g + 2 kG, ... (kG = kWideThreads /
@@ -1572,7 +1666,13 @@ hipError_t launch_decode_d(const DecodeArgs& args, bool bf16, hipStream_t stream
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 mgrid(a.num_q_heads, a.num_seqs);
-  if (a.query_start_loc != nullptr) {
+  if (a.query_start_loc != nullptr && a.num_workers > 8 * a.num_seqs) {
+    // requests split over more than eight workers on average: partials folded by four
+    // lane groups per wavefront
+    hipLaunchKernelGGL((decode_merge_chunk_split_kernel<D>),
+                       dim3(a.num_seqs * a.n_cols, (a.num_q_heads + kMergeHeads - 1) / kMergeHeads),
+                       dim3(64 * kMergeHeads), 0, stream, a);
+  } else if (a.query_start_loc != nullptr) {
     // positions per wavefront: the chunk length's power of two, at most 4
     const int kp = a.n_cols >= 3 ? 4 : a.n_cols;
     const dim3 grid(a.num_seqs * ((a.n_cols + kp - 1) / kp), (a.num_q_heads + kMergeHeads - 1) / kMergeHeads);
